@@ -1,0 +1,351 @@
+"""Pins for the oracle (CPU only).
+
+Every check compares the oracle with something other than itself: a library
+conversion, a second independently written rounding formula, exact integer or
+rational arithmetic in Python, a closed form, or an algebraic identity.  The set
+is chosen so that a dropped term, a wrong sign, a swapped index or a transposed
+operand in the oracle fails at least one of them.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+LAYOUTS = [(la, lb) for la in ("K", "MN") for lb in ("K", "MN")]
+OL = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
+OD = {synth.BF16: oracle.BF16, synth.F16: oracle.F16}
+
+
+def run_oracle(p: synth.Problem, threads=0):
+    return oracle.gemm(p.A, p.B, p.M, p.N, p.K, p.lda, p.ldb, OL[p.layoutA], OL[p.layoutB],
+                       OD[p.dtype], threads)
+
+
+def exact_product(a_vals, b_vals):
+    """Exact C from Python Fractions (a_vals M x K, b_vals K x N floats)."""
+    M, K = len(a_vals), len(a_vals[0]) if a_vals else 0
+    N = len(b_vals[0]) if b_vals else 0
+    return [[sum((Fraction(a_vals[m][k]) * Fraction(b_vals[k][n]) for k in range(K)),
+                 Fraction(0)) for n in range(N)] for m in range(M)]
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_decode_bf16_all_patterns_vs_torch(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, oracle.BF16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_f16_all_patterns_vs_numpy(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, oracle.F16)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ---------------------------------------------------------------- encoders
+
+def _golden_rne():
+    rows = []
+    with open(os.path.join(GOLDEN, "rne_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            fmt, val, bits = line.split()[:3]
+            rows.append((fmt, float.fromhex(val), int(bits, 16)))
+    return rows
+
+
+@pytest.mark.parametrize("fmt,value,bits", _golden_rne())
+def test_encode_golden_cases(oracle_lib, fmt, value, bits):
+    lib = oracle._load()
+    enc = lib.oracle_encode_bf16 if fmt == "bf16" else lib.oracle_encode_f16
+    assert enc(value) == bits, f"{fmt} {value!r}: got {enc(value):#06x}, want {bits:#06x}"
+
+
+def test_encode_special_values(oracle_lib):
+    lib = oracle._load()
+    assert lib.oracle_encode_bf16(float("inf")) == 0x7F80
+    assert lib.oracle_encode_bf16(float("-inf")) == 0xFF80
+    assert lib.oracle_encode_bf16(float("nan")) == 0x7FC0
+    assert lib.oracle_encode_f16(float("inf")) == 0x7C00
+    assert lib.oracle_encode_f16(float("-inf")) == 0xFC00
+    assert lib.oracle_encode_f16(float("nan")) == 0x7E00
+
+
+def _bf16_bit_trick(u32):
+    """Second, independent fp32 -> bf16 RNE: add 0x7FFF plus the kept LSB, shift."""
+    u = u32.astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return r
+
+
+def test_encode_bf16_vs_bit_trick_sampled_fp32(oracle_lib):
+    rng = np.random.default_rng(12345)
+    rand = rng.integers(0, 2 ** 32, size=400_000, dtype=np.uint64).astype(np.uint32)
+    # every exponent with fraction patterns at, just below and just above a tie
+    exps = np.arange(256, dtype=np.uint32) << 23
+    fracs = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0x17FFF, 0x18000, 0x18001, 0x7F7FFF,
+                      0x7F8000, 0x7FFFFF, 0x10000, 0x7FFF00], dtype=np.uint32)
+    struct = (exps[:, None] | fracs[None, :]).reshape(-1)
+    u = np.concatenate([rand, struct, struct | np.uint32(0x80000000)])
+    f = u.view(np.float32)
+    finite = np.isfinite(f)
+    u, f = u[finite], f[finite]
+    got = oracle.encode(f.astype(np.float64), oracle.BF16)
+    want = _bf16_bit_trick(u)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first {u[bad[:5]]}"
+
+
+def test_encode_f16_vs_numpy_sampled(oracle_lib):
+    rng = np.random.default_rng(777)
+    # wide-range random doubles, including the subnormal and overflow ranges
+    mant = rng.uniform(1.0, 2.0, size=200_000)
+    ex = rng.integers(-30, 18, size=mant.size)
+    sign = rng.choice([-1.0, 1.0], size=mant.size)
+    x = sign * np.ldexp(mant, ex)
+    # exact midpoints between adjacent finite fp16 values, and their neighbours
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    x = np.concatenate([x, mid, -mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf)])
+    got = oracle.encode(x, oracle.F16)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first {x[bad[:5]]}"
+
+
+def test_encode_decode_round_trip(oracle_lib):
+    for d in (oracle.BF16, oracle.F16):
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        vals = oracle.decode(bits, d)
+        keep = ~np.isnan(vals)
+        assert np.array_equal(oracle.encode(vals[keep], d), bits[keep])
+
+
+# ---------------------------------------------------------------- GEMM pins
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+def test_identity(oracle_lib, la, lb, dtype):
+    K, N = 37, 29
+    ident = synth.quantize(np.eye(K), dtype)
+    b = synth.quantize(synth.draw(11, K * N, "uniform"), dtype).reshape(K, N)
+    p = synth.layout_problem(ident, b, dtype, la, lb, pad_a=3, pad_b=5)
+    C = run_oracle(p)
+    assert np.array_equal(C, oracle.decode(b, OD[dtype]))
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_permutations(oracle_lib, la, lb):
+    rng = np.random.default_rng(5)
+    M, N, K = 23, 19, 23
+    perm = rng.permutation(K)
+    P = np.zeros((M, K))
+    P[np.arange(M), perm[:M]] = 1.0
+    b = synth.quantize(synth.draw(21, K * N, "normal"), synth.BF16).reshape(K, N)
+    C = run_oracle(synth.layout_problem(synth.quantize(P, synth.BF16), b, synth.BF16, la, lb))
+    bv = oracle.decode(b, oracle.BF16)
+    assert np.array_equal(C, bv[perm[:M], :])        # A = P permutes the rows of B
+    # B = P^T-like column permutation: C = A[:, perm]
+    K2, N2 = 17, 17
+    q = rng.permutation(K2)
+    Q = np.zeros((K2, N2))
+    Q[q, np.arange(N2)] = 1.0
+    a = synth.quantize(synth.draw(22, 13 * K2, "normal"), synth.BF16).reshape(13, K2)
+    C2 = run_oracle(synth.layout_problem(a, synth.quantize(Q, synth.BF16), synth.BF16, la, lb))
+    av = oracle.decode(a, oracle.BF16)
+    assert np.array_equal(C2, av[:, q])
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (7, 5, 3), (64, 33, 257), (3, 2, 4096)])
+def test_all_ones_closed_form(oracle_lib, la, lb, shape):
+    M, N, K = shape
+    for dtype in (synth.BF16, synth.F16):
+        p = synth.make_problem(M, N, K, dtype, la, lb, "ones", 1, 2, pad_a=1, pad_b=2)
+        C = run_oracle(p)
+        assert np.all(C == K)
+
+
+def test_arithmetic_series_closed_form(oracle_lib):
+    # a(m,k) = 1, b(k,n) = k (exact in bf16 for k <= 256): C = K(K-1)/2 for every entry
+    K = 257
+    a = synth.quantize(np.ones((4, K)), synth.BF16)
+    b = synth.quantize(np.repeat(np.arange(K, dtype=np.float64)[:, None], 3, axis=1),
+                       synth.BF16)
+    for la, lb in LAYOUTS:
+        C = run_oracle(synth.layout_problem(a, b, synth.BF16, la, lb))
+        bk = oracle.decode(b[:, 0], oracle.BF16)
+        assert np.all(C == bk.sum())
+    # alternating signs cancel: a = (-1)^k, b = 1
+    a2 = synth.quantize(np.tile((-1.0) ** np.arange(256), (3, 1)), synth.BF16)
+    b2 = synth.quantize(np.ones((256, 5)), synth.BF16)
+    assert np.all(run_oracle(synth.layout_problem(a2, b2, synth.BF16, "K", "MN")) == 0)
+
+
+def test_brute_force_2x2_all_sign_matrices(oracle_lib):
+    vals = (-1.0, 0.0, 1.0)
+    mats = [np.array(v).reshape(2, 2) for v in itertools.product(vals, repeat=4)]
+    qb = [synth.quantize(m, synth.BF16) for m in mats]
+    count = 0
+    for (ma, qa), (mb, qbb) in itertools.product(zip(mats, qb), zip(mats, qb)):
+        p = synth.layout_problem(qa, qbb, synth.BF16, "K", "MN")
+        C = run_oracle(p, threads=1)
+        want = [[int(ma[i][0]) * int(mb[0][j]) + int(ma[i][1]) * int(mb[1][j])
+                 for j in range(2)] for i in range(2)]
+        assert C.tolist() == want
+        count += 1
+    assert count == 6561
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_random_tiny_shapes_vs_exact_rationals(oracle_lib, la, lb):
+    rng = np.random.default_rng(99)
+    for trial in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 6, size=3))
+        dtype = synth.BF16 if trial % 2 else synth.F16
+        p = synth.make_problem(M, N, K, dtype, la, lb, "normal", 100 + trial, 200 + trial,
+                               pad_a=int(rng.integers(0, 3)), pad_b=int(rng.integers(0, 3)))
+        av = oracle.decode(p.A_logical, OD[dtype]).tolist()
+        bv = oracle.decode(p.B_logical, OD[dtype]).tolist()
+        exact = exact_product(av, bv)
+        C = run_oracle(p)
+        for m in range(M):
+            for n in range(N):
+                bound = K * 2.0 ** -53 * sum(abs(av[m][k] * bv[k][n]) for k in range(K))
+                assert abs(Fraction(C[m, n]) - exact[m][n]) <= Fraction(bound)
+        # integer entries: exact equality
+        q = synth.make_problem(M, N, K, dtype, la, lb, "int", 300 + trial, 400 + trial)
+        ai = oracle.decode(q.A_logical, OD[dtype]).astype(int).tolist()
+        bi = oracle.decode(q.B_logical, OD[dtype]).astype(int).tolist()
+        want = [[sum(ai[m][k] * bi[k][n] for k in range(K)) for n in range(N)] for m in range(M)]
+        assert run_oracle(q).tolist() == want
+
+
+def test_nonsquare_matches_python_loop(oracle_lib):
+    # distinct M, N, K and padded leading dims catch swapped indices or ld mix-ups
+    M, N, K = 9, 14, 11
+    for la, lb in LAYOUTS:
+        p = synth.make_problem(M, N, K, synth.BF16, la, lb, "int", 7, 8, pad_a=4, pad_b=6)
+        ai = oracle.decode(p.A_logical, oracle.BF16).astype(int)
+        bi = oracle.decode(p.B_logical, oracle.BF16).astype(int)
+        want = [[int(sum(int(ai[m, k]) * int(bi[k, n]) for k in range(K))) for n in range(N)]
+                for m in range(M)]
+        assert run_oracle(p).tolist() == want
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F16])
+def test_transpose_identity_all_layouts(oracle_lib, dtype):
+    # (AB)^T = B^T A^T: the storage of B read as a left operand is B^T in the
+    # same contiguity flag, and A read as a right operand is A^T.
+    M, N, K = 31, 45, 52
+    for la, lb in LAYOUTS:
+        p = synth.make_problem(M, N, K, dtype, la, lb, "normal", 31, 32, pad_a=2, pad_b=1)
+        C = run_oracle(p)
+        Ct = oracle.gemm(p.B, p.A, N, M, K, p.ldb, p.lda, OL[lb], OL[la], OD[dtype])
+        assert np.array_equal(C.T, Ct)
+
+
+def test_cross_layout_bit_identical(oracle_lib):
+    a, b = synth.make_logical(40, 24, 72, synth.BF16, "uniform", 41, 42)
+    outs = [run_oracle(synth.layout_problem(a, b, synth.BF16, la, lb, 3, 5)) for la, lb in LAYOUTS]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_linearity_integer(oracle_lib):
+    M, N, K = 12, 10, 33
+    a, b1 = synth.make_logical(M, N, K, synth.BF16, "int", 51, 52)
+    _, b2 = synth.make_logical(M, N, K, synth.BF16, "int", 53, 54)
+    bsum = synth.quantize(oracle.decode(b1, oracle.BF16) + oracle.decode(b2, oracle.BF16),
+                          synth.BF16)
+    c1 = run_oracle(synth.layout_problem(a, b1, synth.BF16, "K", "MN"))
+    c2 = run_oracle(synth.layout_problem(a, b2, synth.BF16, "K", "MN"))
+    cs = run_oracle(synth.layout_problem(a, bsum, synth.BF16, "K", "MN"))
+    assert np.array_equal(cs, c1 + c2)
+    # negating A negates C
+    aneg = synth.quantize(-oracle.decode(a, oracle.BF16), synth.BF16)
+    cn = run_oracle(synth.layout_problem(aneg, b1, synth.BF16, "K", "MN"))
+    assert np.array_equal(cn, -c1)
+
+
+def test_rows_and_entries_agree_with_full(oracle_lib):
+    M, N, K = 50, 37, 91
+    for la, lb in LAYOUTS:
+        p = synth.make_problem(M, N, K, synth.F16, la, lb, "normal", 61, 62, 0.1, pad_a=1)
+        C = run_oracle(p)
+        R = oracle.gemm_rows(p.A, p.B, M, N, K, p.lda, p.ldb, OL[la], OL[lb], oracle.F16, 7, 29)
+        assert np.array_equal(R, C[7:29])
+        rng = np.random.default_rng(3)
+        rows = rng.integers(0, M, 200)
+        cols = rng.integers(0, N, 200)
+        E = oracle.gemm_entries(p.A, p.B, M, N, K, p.lda, p.ldb, OL[la], OL[lb], oracle.F16,
+                                rows, cols)
+        assert np.array_equal(E, C[rows, cols])
+
+
+def test_thread_count_does_not_change_result(oracle_lib):
+    p = synth.make_problem(33, 65, 129, synth.BF16, "K", "MN", "normal", 71, 72)
+    assert np.array_equal(run_oracle(p, threads=1), run_oracle(p, threads=3))
+
+
+def test_padding_is_never_read(oracle_lib):
+    # synth fills padding with NaN; any read of it would poison the sum
+    p = synth.make_problem(20, 30, 40, synth.BF16, "MN", "K", "uniform", 81, 82, pad_a=8, pad_b=8)
+    assert np.all(np.isfinite(run_oracle(p)))
+
+
+def test_degenerate_shapes(oracle_lib):
+    z = np.zeros(1, dtype=np.uint16)
+    C = oracle.gemm(z, z, 3, 4, 0, 1, 4, oracle.K_CONTIG, oracle.MN_CONTIG, oracle.BF16)
+    assert C.shape == (3, 4) and np.all(C == 0)        # empty sum
+    C = oracle.gemm(z, z, 0, 4, 5, 5, 4, oracle.K_CONTIG, oracle.MN_CONTIG, oracle.BF16)
+    assert C.shape == (0, 4)
+
+
+def test_invalid_arguments_rejected(oracle_lib):
+    z = np.zeros(64, dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm(z, z, 4, 4, 4, 3, 4, oracle.K_CONTIG, oracle.MN_CONTIG, oracle.BF16)  # lda < K
+    with pytest.raises(ValueError):
+        oracle.gemm(z, z, 4, 4, 4, 4, 4, 2, oracle.MN_CONTIG, oracle.BF16)
+    with pytest.raises(ValueError):
+        oracle.gemm(z, z, 4, 4, 4, 4, 4, oracle.K_CONTIG, oracle.MN_CONTIG, 7)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_splitmix64_reference_values():
+    # SplitMix64 with state 0: first outputs published with the algorithm
+    # (Vigna's reference implementation, seed 0).
+    x = synth.splitmix64(0, 3)
+    assert [int(v) for v in x] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_generator_distributions():
+    u = synth.draw(1, 100_000, "uniform")
+    assert u.min() >= -1 and u.max() < 1 and abs(u.mean()) < 0.01
+    n = synth.draw(2, 100_000, "normal")
+    assert abs(n.mean()) < 0.02 and abs(n.std() - 1) < 0.02
+    i = synth.draw(3, 10_000, "int")
+    assert set(np.unique(i).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
