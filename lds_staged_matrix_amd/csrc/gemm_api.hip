@@ -1,0 +1,171 @@
+// gemm_api.hip -- the C ABI declared in include/lds_gemm.h: argument
+// validation, choice of tile shape, and the kernel launch on the caller's
+// stream.  Every launched kernel comes from gemm_kernel.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "gemm_kernel.h"
+#include "lds_gemm.h"
+
+struct gemm_ctx {
+  int device;
+};
+
+namespace lsm {
+
+// Tile shapes.  GROUP_M is the number of tile rows walked together so that
+// workgroups resident on one XCD share A and B panels in its L2.
+//   Big:    256 x 256 x 64, 8 waves (2 per SIMD), each wave 128 x 64.
+//           LDS 2 stages x 64 KiB = 128 KiB.
+//   Mid:    128 x 128 x 64, 4 waves of 64 x 64.  LDS 64 KiB.
+//   Small:  64 x 64 x 64, 4 waves of 32 x 32.  LDS 32 KiB.
+//   Skinny: 32 x 64 x 64, 2 waves of 32 x 32 for M <= 32.  LDS 24 KiB.
+using Big = Tile<256, 256, 64, 2, 4, 8>;
+using Mid = Tile<128, 128, 64, 2, 2, 8>;
+using Small = Tile<64, 64, 64, 2, 2, 4>;
+using Skinny = Tile<32, 64, 64, 1, 2, 8>;
+
+struct Args {
+  const uint16_t *A;
+  const uint16_t *B;
+  void *C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+};
+
+template <class T, int LA, int LB, int IN, int OUT>
+static hipError_t launch(const Args &a, hipStream_t stream) {
+  int tiles_m = (a.M + T::BM - 1) / T::BM;
+  int tiles_n = (a.N + T::BN - 1) / T::BN;
+  const uint16_t *A = a.A, *B = a.B;
+  void *C = a.C;
+  int M = a.M, N = a.N, K = a.K;
+  int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
+  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n};
+  return hipLaunchKernel((const void *)lds_gemm_kernel<T, LA, LB, IN, OUT>,
+                         dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
+}
+
+template <class T, int IN, int OUT>
+static hipError_t launch_layout(const Args &a, int la, int lb, hipStream_t s) {
+  if (la == KC && lb == KC) return launch<T, KC, KC, IN, OUT>(a, s);
+  if (la == KC && lb == MNC) return launch<T, KC, MNC, IN, OUT>(a, s);
+  if (la == MNC && lb == KC) return launch<T, MNC, KC, IN, OUT>(a, s);
+  return launch<T, MNC, MNC, IN, OUT>(a, s);
+}
+
+template <class T>
+static hipError_t launch_dtype(const Args &a, int la, int lb, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case GEMM_BF16_F32: return launch_layout<T, IN_BF16, OUT_F32>(a, la, lb, s);
+    case GEMM_BF16_BF16: return launch_layout<T, IN_BF16, OUT_BF16>(a, la, lb, s);
+    case GEMM_F16_F16: return launch_layout<T, IN_F16, OUT_F16>(a, la, lb, s);
+    default: return launch_layout<T, IN_F16, OUT_F32>(a, la, lb, s);
+  }
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape classes.  The big tile when it still gives every CU at least one
+// workgroup, else the 128 tile when that gives at least a quarter of the
+// CUs work, else the 64 tile; M <= 32 takes the skinny tile.
+static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t s) {
+  if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
+  if (ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256) return launch_dtype<Big>(a, la, lb, dtype, s);
+  if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64) return launch_dtype<Mid>(a, la, lb, dtype, s);
+  return launch_dtype<Small>(a, la, lb, dtype, s);
+}
+
+static bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
+}
+
+}  // namespace lsm
+
+extern "C" {
+
+int gemm_create(gemm_handle_t *out) {
+  if (!out) return GEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_DEVICE;
+  gemm_ctx *h = new (std::nothrow) gemm_ctx{dev};
+  if (!h) return GEMM_ERR_DEVICE;
+  *out = h;
+  return GEMM_OK;
+}
+
+int gemm_destroy(gemm_handle_t h) {
+  delete h;
+  return GEMM_OK;
+}
+
+const char *gemm_status_str(int status) {
+  switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported argument (alignment or size)";
+    case GEMM_ERR_DEVICE: return "device is not a usable gfx950 device";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, int64_t N,
+             int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int layoutA, int layoutB,
+             int dtype, hipStream_t stream) {
+  using namespace lsm;
+  if (!h) return GEMM_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+  if ((layoutA != GEMM_K_CONTIG && layoutA != GEMM_MN_CONTIG) ||
+      (layoutB != GEMM_K_CONTIG && layoutB != GEMM_MN_CONTIG))
+    return GEMM_ERR_INVALID_ARG;
+  if (dtype < GEMM_BF16_F32 || dtype > GEMM_F16_F32) return GEMM_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return GEMM_OK;
+  if (!C || (K > 0 && (!A || !B))) return GEMM_ERR_INVALID_ARG;
+
+  const int64_t a_outer = layoutA == GEMM_K_CONTIG ? M : K;
+  const int64_t a_inner = layoutA == GEMM_K_CONTIG ? K : M;
+  const int64_t b_outer = layoutB == GEMM_MN_CONTIG ? K : N;
+  const int64_t b_inner = layoutB == GEMM_MN_CONTIG ? N : K;
+  if (lda < a_inner || ldb < b_inner || ldc < N || lda < 1 || ldb < 1)
+    return GEMM_ERR_INVALID_ARG;
+
+  const int64_t kMaxDim = (int64_t)1 << 30;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+  // the grid of the smallest tile (32 x 64) must fit a 31-bit workgroup count
+  if (ceil_div(M, 32) * ceil_div(N, 64) >= ((int64_t)1 << 31)) return GEMM_ERR_UNSUPPORTED;
+  if (lda >= ((int64_t)1 << 40) || ldb >= ((int64_t)1 << 40) || ldc >= ((int64_t)1 << 40))
+    return GEMM_ERR_UNSUPPORTED;
+  const int64_t out_size = (dtype == GEMM_BF16_F32 || dtype == GEMM_F16_F32) ? 4 : 2;
+  if (K > 0) {
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || (lda & 7) || (ldb & 7))
+      return GEMM_ERR_UNSUPPORTED;
+  }
+  if ((uintptr_t)C & (uintptr_t)(out_size - 1)) return GEMM_ERR_UNSUPPORTED;
+
+  const int64_t c_bytes = ((M - 1) * ldc + N) * out_size;
+  if (K > 0) {
+    const int64_t a_bytes = ((a_outer - 1) * lda + a_inner) * 2;
+    const int64_t b_bytes = ((b_outer - 1) * ldb + b_inner) * 2;
+    if (ranges_overlap(C, c_bytes, A, a_bytes) || ranges_overlap(C, c_bytes, B, b_bytes))
+      return GEMM_ERR_INVALID_ARG;
+  }
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return GEMM_ERR_DEVICE;
+
+  const Args args{(const uint16_t *)A, (const uint16_t *)B, C, (int)M, (int)N, (int)K,
+                  lda, ldb, ldc};
+  if (dispatch(args, layoutA, layoutB, dtype, stream) != hipSuccess) return GEMM_ERR_LAUNCH;
+  return GEMM_OK;
+}
+
+}  // extern "C"

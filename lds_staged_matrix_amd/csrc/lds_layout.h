@@ -1,0 +1,130 @@
+// lds_layout.h -- LDS tile layouts and per-lane LDS addresses of the GEMM.
+//
+// Pure integer functions, usable on the host (the bank-conflict model in the
+// tests evaluates exactly these) and on the device (the kernel computes every
+// LDS address with them).
+//
+// gfx950 LDS: 64 banks of 4 bytes, bank = (byte_address / 4) mod 64, so one
+// 256-byte line touches every bank once ("Lds Optimization", section "LDS
+// Architecture on CDNA4 (gfx950)", Hardware Facts).  Addresses that differ by
+// a multiple of 256 bytes share banks; a 256-byte row stride is a 64-way
+// conflict for a column walk (same page, "Impact on Bank Conflict Analysis").
+// The fix used here is an XOR swizzle of the 16-byte chunk index with bits of
+// the row index (same page, "Optimization Method 1: Swizzle Layout"), applied
+// identically on the write and the read side (same page, "Verification
+// Checklist", item 1).  The swizzle unit is a whole 16-byte chunk, never less
+// than one lane's access, so every ds_write_b128 / ds_read_b128 stays one
+// contiguous 16-byte vector ("Fix LDS vectorization logic to allow for bank
+// conflict resolution when kPack > kPerThread": a write that is neither
+// vectorised nor rotated is the 8-way case).
+//
+// Two tile kinds:
+//  * K-contiguous tile: rows are M (or N) indices, each row holds the tile's
+//    K extent contiguously (row_bytes = 2*BK).  Read with ds_read_b128: one
+//    lane takes 8 consecutive k of one row.  A 16-lane phase reads 16
+//    consecutive rows at one logical chunk; the swizzle puts them in 16
+//    distinct 16-byte bank groups.
+//  * MN-contiguous tile: rows are k indices, each row holds the tile's M (or
+//    N) extent contiguously.  Read with ds_read_b64_tr_b16 ("Lds
+//    Optimization", section "MFMA Transpose Load from LDS (gfx950 only)"): a
+//    lane reads 4 consecutive M/N values of one k row and the hardware
+//    redistributes them so each lane ends up with 4 consecutive k of one
+//    column.  Bank conflicts are decided by the source addresses ("A Deep
+//    Dive into LDS Optimizations on AMD Instinct MI450 GPUs", Part I, end of
+//    "What Does ds_load_tr Do?").
+//
+// Lane redistribution of ds_read_b64_tr_b16 on gfx950, measured with a probe
+// kernel: inside each aligned group of 16 lanes, destination lane d receives,
+// as its element j (j = 0..3), element (d & 3) of source lane (d >> 2) + 4*j.
+// Hence, for destination lane d to hold column c0 + d of rows r0..r0+3,
+// source lane s reads row r0 + (s >> 2), columns c0 + 4*(s & 3) .. +3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace lsm {
+
+// ---------------------------------------------------------------- swizzles
+
+// XOR applied to the chunk index of row `row` of a K-contiguous tile.
+__host__ __device__ constexpr int kc_swizzle(int row, int row_bytes) {
+  // rows per 256-byte bank line and chunks per row
+  return row_bytes >= 256 ? (row & 15)
+                          : ((row / (256 / row_bytes)) & (row_bytes / 16 - 1));
+}
+
+// XOR applied to the chunk index of k-row `k` of an MN-contiguous tile: the
+// four k rows read by one 32-lane transposed-read phase land in four distinct
+// 64-byte quarters of the bank line.
+__host__ __device__ constexpr int mn_swizzle(int k, int row_bytes) {
+  return row_bytes >= 256 ? 4 * (k & 3) : (row_bytes == 128 ? 4 * ((k >> 1) & 1) : 0);
+}
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
+__host__ __device__ constexpr int kc_chunk_offset(int row, int chunk, int row_bytes) {
+  return row * row_bytes + 16 * (chunk ^ kc_swizzle(row, row_bytes));
+}
+
+// Byte offset of 16-byte chunk `chunk` of k-row `k` in an MN-contiguous tile.
+__host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_bytes) {
+  return k * row_bytes + 16 * (chunk ^ mn_swizzle(k, row_bytes));
+}
+
+// ---------------------------------------------------------------- loader
+
+// The global->LDS loader splits a tile of `rows` x `row_bytes` into 16-byte
+// chunks numbered row-major; chunk id = thread + i * threads for load i.
+// Consecutive lanes take consecutive chunks of a row, so a wave's global
+// access is contiguous along the operand's unit-stride dimension.
+__host__ __device__ constexpr int loader_row(int id, int row_bytes) { return id / (row_bytes / 16); }
+__host__ __device__ constexpr int loader_chunk(int id, int row_bytes) { return id % (row_bytes / 16); }
+
+__host__ __device__ constexpr int loader_lds_offset(int id, int row_bytes, bool k_contig) {
+  return k_contig ? kc_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes)
+                  : mn_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes);
+}
+
+// ---------------------------------------------------------------- fragment reads
+//
+// Fragments of v_mfma_f32_32x32x16_{bf16,f16} (layout checked with a probe):
+// lane l holds operand row/column (l & 31) and k = 8*(l >> 5) + i, i = 0..7,
+// for both A and B.  `base` is the first M/N index of the 32-wide fragment
+// inside the tile, `kk` the 16-deep k step inside the tile.
+
+// K-contiguous operand: one ds_read_b128 per fragment.
+__host__ __device__ constexpr int frag_kc_offset(int lane, int base, int kk, int row_bytes) {
+  return kc_chunk_offset(base + (lane & 31), 2 * kk + (lane >> 5), row_bytes);
+}
+
+// MN-contiguous operand: two ds_read_b64_tr_b16 per fragment, half h = 0, 1
+// delivering k = 8*(l >> 5) + 4*h + 0..3.  Source lane l reads k-row
+// 16*kk + 8*(l >> 5) + 4*h + ((l >> 2) & 3) at columns
+// base + 16*((l >> 4) & 1) + 4*(l & 3) .. +3.
+__host__ __device__ constexpr int frag_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
+  return mn_chunk_offset(16 * kk + 8 * (lane >> 5) + 4 * h + ((lane >> 2) & 3),
+                         (base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) / 8, row_bytes) +
+         8 * (lane & 1);
+}
+
+// ---------------------------------------------------------------- workgroup -> tile
+//
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b on XCD b mod 8),
+// and each XCD has its own L2.  The logical tile id gives each XCD one
+// contiguous range of ids, then walks tiles in groups of `group_m` tile rows
+// so the workgroups resident on one XCD at a time share A and B panels.
+__host__ __device__ constexpr int xcd_logical_id(int bid, int nwg) {
+  return (bid & 7) * (nwg >> 3) + ((bid & 7) < (nwg & 7) ? (bid & 7) : (nwg & 7)) + (bid >> 3);
+}
+
+__host__ __device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn) {
+  const int width = group_m * tiles_n;
+  const int group = lid / width;
+  const int first_m = group * group_m;
+  const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+  const int in = lid - group * width;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+}  // namespace lsm

@@ -1,0 +1,118 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+that include/*.h declares, and validates arguments before touching a device.
+No GPU compute is called here."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import lds_staged_matrix_amd as lsm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lsm.library_path()):
+        from lds_staged_matrix_amd import build
+        build.build()
+    return lsm.load_library()
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", text,
+                            flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    assert set(declared_functions()) >= {"gemm_create", "gemm_run", "gemm_destroy",
+                                         "gemm_status_str"}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lsm.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in include/ but not exported"
+        assert hasattr(lib, name)
+    assert set(lsm.EXPORTED_SYMBOLS) <= exported
+
+
+def test_library_is_gfx950_code_object(lib):
+    # the device code object embedded in the library targets gfx950
+    data = open(lsm.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lib):
+    assert lsm.gemm_status_str(lsm.GEMM_OK) == "success"
+    for st in range(1, 5):
+        assert lsm.gemm_status_str(st) != "unknown status"
+    assert lsm.gemm_status_str(99) == "unknown status"
+
+
+def test_destroy_null_is_ok(lib):
+    assert lsm.gemm_destroy(None) == lsm.GEMM_OK
+
+
+@pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES") is None and
+                    os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK),
+                    reason="a GPU may be present; this checks the no-device path")
+def test_create_without_device_fails_cleanly(lib):
+    h = ctypes.c_void_p()
+    st = lib.gemm_create(ctypes.byref(h))
+    assert st == lsm.GEMM_ERR_DEVICE and not h.value
+    assert lib.gemm_create(None) == lsm.GEMM_ERR_INVALID_ARG
+
+
+def test_run_with_null_handle(lib):
+    assert lsm.gemm_run(None, 16, 16, 16, 1, 1, 1, 1, 1, 1, 0, 1, 0) == lsm.GEMM_ERR_INVALID_ARG
+
+
+# A stand-in handle: validation returns before the handle is dereferenced; a
+# request that passes validation reaches the device check, which fails on a
+# machine with no device (or whose device is not the handle's).
+_FAKE_DEVICE = ctypes.c_int(1 << 20)
+FAKE = ctypes.cast(ctypes.pointer(_FAKE_DEVICE), ctypes.c_void_p)
+A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addresses
+
+
+@pytest.mark.parametrize("args,status", [
+    # (A, B, C, M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype)
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),       # valid
+    ((A0, B0, C0, -1, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 16, 16, -3, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 2, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, -1, 0), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 4), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 0, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_OK),               # empty: no-op
+    ((A0, B0, C0, 16, 0, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_OK),
+    ((A0, B0, 0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),   # NULL C
+    ((0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),   # NULL A
+    ((0, 0, C0, 16, 16, 0, 8, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),          # K=0 needs no A/B
+    ((A0, B0, C0, 16, 16, 16, 8, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),   # lda < K
+    ((A0, B0, C0, 16, 24, 16, 16, 16, 24, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # ldb < N
+    ((A0, B0, C0, 16, 24, 16, 16, 24, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # ldc < N
+    ((A0, B0, C0, 24, 16, 16, 16, 16, 16, 1, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # lda < M (MN)
+    ((A0, B0, C0, 16, 24, 16, 16, 8, 24, 0, 0, 0), lsm.GEMM_ERR_INVALID_ARG),   # ldb < K (K)
+    ((A0 + 2, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # A align
+    ((A0, B0 + 8, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # B align
+    ((A0, B0, C0 + 2, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # C align f32
+    ((A0, B0, C0 + 2, 16, 16, 16, 16, 16, 16, 0, 1, 1), lsm.GEMM_ERR_DEVICE),       # ok for bf16
+    ((A0, B0, C0, 16, 16, 12, 12, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # lda % 8
+    ((A0, B0, C0, 16, 16, 16, 16, 20, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # ldb % 8
+    ((A0, B0, C0, 1 << 30, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
+    ((A0, B0, A0 + 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C in A
+    ((A0, B0, B0 - 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C over B
+    ((A0, B0, A0 + 512, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),    # just past A
+])
+def test_validation(lib, args, status):
+    assert lsm.gemm_run(FAKE, *args) == status
