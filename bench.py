@@ -1,0 +1,240 @@
+"""Benchmark of the LDS-staged GEMM on one MI355X.
+
+One step = one C <- A*B through the C ABI on the workload's synthetic,
+HBM-resident inputs.  The default workload is bf16 M=N=K=8192, A K-contiguous,
+B N-contiguous (transposed-LDS-read path), fp32 output.
+
+Prints ONE JSON line on stdout.  Extra per-run detail goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --profile-run      # a few launches only, for rocprofv3
+  python bench.py --copy-calibration # one plain 1 GiB device copy, for rocprofv3 --pmc
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "bf16 GEMM TFLOP/s + % of MFMA peak; LDS bank-conflict rate (1 MI355X)"
+# MI355X dense MFMA peak for bf16/fp16 inputs: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 2516.6
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "bf16_8192_nn_f32"
+KERNEL_SOURCES = ["lds_staged_matrix_amd/csrc/gemm_kernel.h",
+                  "lds_staged_matrix_amd/csrc/lds_layout.h",
+                  "lds_staged_matrix_amd/csrc/gemm_api.hip"]
+DTYPE_CODE = {("bf16", "f32"): 0, ("bf16", "bf16"): 1, ("f16", "f16"): 2, ("f16", "f32"): 3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def make_inputs(w, layout):
+    import torch
+    la, lb = layout
+    p = synth.make_problem(w["M"], w["N"], w["K"], w["dtype"], la, lb, w["dist"], w["seeds"][0],
+                           w["seeds"][1], w["scale"])
+    A = torch.from_numpy(p.A.view(np.int16)).cuda()
+    B = torch.from_numpy(p.B.view(np.int16)).cuda()
+    return p, A, B
+
+
+def cpu_baseline(p, rows):
+    """The oracle, as it is, on `rows` full rows of C of the same problem."""
+    import oracle
+    ol = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
+    od = {synth.BF16: oracle.BF16, synth.F16: oracle.F16}
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.gemm_rows(p.A, p.B, p.M, p.N, p.K, p.lda, p.ldb, ol[p.layoutA], ol[p.layoutB],
+                     od[p.dtype], 0, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * p.N * p.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle fp64 m->k->n loop on rows 0..{rows - 1} of the same "
+                      f"{p.M}x{p.N}x{p.K} problem ({rows * p.N} outputs), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--layout", default=None, help="e.g. K,MN (A contiguity, B contiguity)")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--flushed", action="store_true",
+                    help="also time 20 launches with a 1 GiB cache flush before each")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build is a single-GPU kernel library "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lds_staged_matrix_amd as lsm
+
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        return
+
+    w = dict(synth.WORKLOADS[args.workload])
+    layout = tuple(args.layout.split(",")) if args.layout else w["layouts"][0]
+    gd = DTYPE_CODE[(w["dtype"], w["out"])]
+    M, N, K = w["M"], w["N"], w["K"]
+    log(f"workload {args.workload} layout {layout} M={M} N={N} K={K}")
+    p, A, B = make_inputs(w, layout)
+    C = torch.empty(M * N, dtype=torch.float32 if w["out"] == "f32" else torch.int16,
+                    device="cuda")
+    h = lsm.gemm_create()
+    stream = torch.cuda.current_stream()
+    la = lsm.GEMM_K_CONTIG if layout[0] == "K" else lsm.GEMM_MN_CONTIG
+    lb = lsm.GEMM_K_CONTIG if layout[1] == "K" else lsm.GEMM_MN_CONTIG
+
+    def step():
+        st = lsm.gemm_run(h, A, B, C, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream)
+        if st != lsm.GEMM_OK:
+            raise lsm.GemmError(st, "gemm_run")
+
+    if args.profile_run:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        log("profile run: 5 launches done")
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` launches back to back; a HIP event pair on
+    # the launch stream around every launch gives the kernel's own duration.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    # Same kernel with the caches flushed before each launch (the pages'
+    # method), timed per launch outside the flush.
+    fl_ms = []
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flushed else None
+    for i in range(20 if args.flushed else 0):
+        flush.fill_(i & 0xFF)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        fl_ms.append(s.elapsed_time(e))
+    del flush
+
+    flops = 2.0 * M * N * K
+    out_bytes = 4 if w["out"] == "f32" else 2
+    alg_bytes = 2.0 * (M * K + K * N) + out_bytes * M * N
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kavg = float(kern_ms.mean())
+    hbm_bound = flops / alg_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved = alg_bytes / (kavg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flops / (kavg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    src_hash = kernel_source_hash()
+    roof["traffic"] = read_traffic(args.workload, src_hash) if layout == tuple(w["layouts"][0]) \
+        else None
+
+    log(f"kernel ms: mean {kavg:.4f} median {np.median(kern_ms):.4f} min {kern_ms.min():.4f}; "
+        f"flushed-cache median {np.median(fl_ms) if fl_ms else float('nan'):.4f} ms; "
+        f"wall per step {ms_per_step:.4f} ms")
+    log(f"kernel TFLOP/s {flops / (kavg * 1e-3) / 1e12:.1f}, "
+        f"{flops / (kavg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100:.1f}% of dense bf16 peak; "
+        f"algorithmic GB/s {alg_bytes / (kavg * 1e-3) / 1e9:.1f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = max(1, min(args.cpu_rows, M))
+        cpu = cpu_baseline(p, rows)
+        log(f"cpu baseline: {cpu}")
+
+    unit = "TFLOP/s"
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w["dtype"] == synth.BF16 else "f16", "data": "synthetic",
+        "config": {"workload": f"{w['dtype']} GEMM M={M} N={N} K={K}, A "
+                               f"{'K' if layout[0] == 'K' else 'M'}-contiguous, B "
+                               f"{'K' if layout[1] == 'K' else 'N'}-contiguous, {w['out']} output, "
+                               f"fp32 accumulation", "name": args.workload,
+                   "M": M, "N": N, "K": K, "layout": "".join("N" if x == ("K" if i == 0 else "MN")
+                                                          else "T" for i, x in enumerate(layout)),
+                   "inputs": f"{w['dist']} x{w['scale']} seeds {w['seeds']}",
+                   "kernel_ms_mean": round(kavg, 5), "kernel_ms_flushed_median":
+                       round(float(np.median(fl_ms)), 5) if fl_ms else None,
+                   "kernel_source_hash": src_hash},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    lsm.gemm_destroy(h)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
