@@ -8,6 +8,7 @@
 #include <new>
 
 #include "gemm_kernel.h"
+#include "gemm_kernel_dma.h"
 #include "lds_gemm.h"
 
 struct gemm_ctx {
@@ -27,6 +28,11 @@ using Big = Tile<256, 256, 64, 2, 4, 8>;
 using Mid = Tile<128, 128, 64, 2, 2, 8>;
 using Small = Tile<64, 64, 64, 2, 2, 4>;
 using Skinny = Tile<32, 64, 64, 1, 2, 8>;
+// Direct-to-LDS kernel shapes: 4 waves (one per SIMD).
+//   DmaBig: 256 x 256 x 64, wave tile 128 x 128, LDS 2 x 64 KiB.
+//   DmaMid: 128 x 128 x 64, wave tile 64 x 64, LDS 2 x 32 KiB.
+using DmaBig = Tile<256, 256, 64, 2, 2, 8>;
+using DmaMid = Tile<128, 128, 64, 2, 2, 8>;
 
 struct Args {
   const uint16_t *A;
@@ -34,7 +40,22 @@ struct Args {
   void *C;
   int M, N, K;
   int64_t lda, ldb, ldc;
+  uint32_t a_bytes, b_bytes;   // operand footprints (used by the direct-to-LDS kernel)
 };
+
+template <class T, int LA, int LB, int IN, int OUT>
+static hipError_t launch_dma(const Args &a, hipStream_t stream) {
+  int tiles_m = (a.M + T::BM - 1) / T::BM;
+  int tiles_n = (a.N + T::BN - 1) / T::BN;
+  const uint16_t *A = a.A, *B = a.B;
+  void *C = a.C;
+  int M = a.M, N = a.N, K = a.K;
+  int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
+  uint32_t ab = a.a_bytes, bb = a.b_bytes;
+  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb};
+  return hipLaunchKernel((const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT>,
+                         dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
+}
 
 template <class T, int LA, int LB, int IN, int OUT>
 static hipError_t launch(const Args &a, hipStream_t stream) {
@@ -49,31 +70,57 @@ static hipError_t launch(const Args &a, hipStream_t stream) {
                          dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
 }
 
-template <class T, int IN, int OUT>
-static hipError_t launch_layout(const Args &a, int la, int lb, hipStream_t s) {
-  if (la == KC && lb == KC) return launch<T, KC, KC, IN, OUT>(a, s);
-  if (la == KC && lb == MNC) return launch<T, KC, MNC, IN, OUT>(a, s);
-  if (la == MNC && lb == KC) return launch<T, MNC, KC, IN, OUT>(a, s);
-  return launch<T, MNC, MNC, IN, OUT>(a, s);
+template <class T, bool DMA, int LA, int LB, int IN, int OUT>
+static hipError_t launch_kind(const Args &a, hipStream_t s) {
+  if constexpr (DMA)
+    return launch_dma<T, LA, LB, IN, OUT>(a, s);
+  else
+    return launch<T, LA, LB, IN, OUT>(a, s);
 }
 
-template <class T>
+template <class T, bool DMA, int IN, int OUT>
+static hipError_t launch_layout(const Args &a, int la, int lb, hipStream_t s) {
+  if (la == KC && lb == KC) return launch_kind<T, DMA, KC, KC, IN, OUT>(a, s);
+  if (la == KC && lb == MNC) return launch_kind<T, DMA, KC, MNC, IN, OUT>(a, s);
+  if (la == MNC && lb == KC) return launch_kind<T, DMA, MNC, KC, IN, OUT>(a, s);
+  return launch_kind<T, DMA, MNC, MNC, IN, OUT>(a, s);
+}
+
+template <class T, bool DMA = false>
 static hipError_t launch_dtype(const Args &a, int la, int lb, int dtype, hipStream_t s) {
   switch (dtype) {
-    case GEMM_BF16_F32: return launch_layout<T, IN_BF16, OUT_F32>(a, la, lb, s);
-    case GEMM_BF16_BF16: return launch_layout<T, IN_BF16, OUT_BF16>(a, la, lb, s);
-    case GEMM_F16_F16: return launch_layout<T, IN_F16, OUT_F16>(a, la, lb, s);
-    default: return launch_layout<T, IN_F16, OUT_F32>(a, la, lb, s);
+    case GEMM_BF16_F32: return launch_layout<T, DMA, IN_BF16, OUT_F32>(a, la, lb, s);
+    case GEMM_BF16_BF16: return launch_layout<T, DMA, IN_BF16, OUT_BF16>(a, la, lb, s);
+    case GEMM_F16_F16: return launch_layout<T, DMA, IN_F16, OUT_F16>(a, la, lb, s);
+    default: return launch_layout<T, DMA, IN_F16, OUT_F32>(a, la, lb, s);
   }
 }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The direct-to-LDS kernel needs whole 16-byte chunks along each operand's
+// contiguous dimension, and byte offsets (footprint plus one tile of rows of
+// overhang, plus a K advance) below 2^31 for its 32-bit buffer offsets.
+static bool dma_ok(const Args &a, int la, int lb) {
+  const int64_t a_inner = la == KC ? a.K : a.M, a_outer = la == KC ? a.M : a.K;
+  const int64_t b_inner = lb == MNC ? a.N : a.K, b_outer = lb == MNC ? a.K : a.N;
+  const int64_t lim = (int64_t)1 << 31;
+  return a_inner % 8 == 0 && b_inner % 8 == 0 &&
+         (a_outer + 512) * a.lda * 2 + 2 * (int64_t)a.K < lim &&
+         (b_outer + 512) * a.ldb * 2 + 2 * (int64_t)a.K < lim;
+}
+
 // Shape classes.  The big tile when it still gives every CU at least one
 // workgroup, else the 128 tile when that gives at least a quarter of the
-// CUs work, else the 64 tile; M <= 32 takes the skinny tile.
+// CUs work, else the 64 tile; M <= 32 takes the skinny tile.  Big and mid
+// shapes take the direct-to-LDS kernel when dma_ok() holds.
 static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t s) {
   if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
+  const bool dma = dma_ok(a, la, lb);
+  if (dma && ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256)
+    return launch_dtype<DmaBig, true>(a, la, lb, dtype, s);
+  if (dma && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64)
+    return launch_dtype<DmaMid, true>(a, la, lb, dtype, s);
   if (ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256) return launch_dtype<Big>(a, la, lb, dtype, s);
   if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64) return launch_dtype<Mid>(a, la, lb, dtype, s);
   return launch_dtype<Small>(a, la, lb, dtype, s);
@@ -162,8 +209,11 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, 
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return GEMM_ERR_DEVICE;
 
+  const int64_t a_fp = K > 0 ? ((a_outer - 1) * lda + a_inner) * 2 : 0;
+  const int64_t b_fp = K > 0 ? ((b_outer - 1) * ldb + b_inner) * 2 : 0;
   const Args args{(const uint16_t *)A, (const uint16_t *)B, C, (int)M, (int)N, (int)K,
-                  lda, ldb, ldc};
+                  lda, ldb, ldc, (uint32_t)(a_fp < ((int64_t)1 << 31) ? a_fp : 0),
+                  (uint32_t)(b_fp < ((int64_t)1 << 31) ? b_fp : 0)};
   if (dispatch(args, layoutA, layoutB, dtype, stream) != hipSuccess) return GEMM_ERR_LAUNCH;
   return GEMM_OK;
 }

@@ -1,0 +1,129 @@
+// gemm_common.h -- pieces shared by the GEMM kernels: vector types, tile
+// geometry, the MFMA micro-kernel, LDS fragment reads and the epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_layout.h"
+
+namespace lsm {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef _Float16 v8f16 __attribute__((ext_vector_type(8)));
+typedef float v16f32 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+enum { KC = 0, MNC = 1 };                       // operand contiguity, values of enum gemm_layout
+enum { IN_BF16 = 0, IN_F16 = 1 };
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WM = WM_, WN = WN_;                // wave grid inside the workgroup
+  static constexpr int GROUP_M = GROUP_M_;                // tile rows per L2 group
+  static constexpr int NT = WM * WN * 64;                  // threads per workgroup
+  static constexpr int TM = BM / WM, TN = BN / WN;         // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;         // 32x32 fragments per wave
+  static constexpr int KSTEPS = BK / 16;                   // MFMA k steps per K tile
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(BK % 16 == 0, "BK must be a multiple of 16");
+};
+
+// Geometry of one operand's LDS tile.  MN is the tile's M (for A) or N (for
+// B) extent.  K-contiguous: MN rows of BK elements.  MN-contiguous: BK rows of
+// MN elements.  "outer" is the strided dimension of the operand in memory,
+// "inner" its unit-stride dimension.  The tile is filled in rounds of NT
+// 16-byte chunks: chunk id = thread + round * NT, numbered row-major.
+template <int MN, int BK, int LAYOUT, int NT>
+struct OperandTile {
+  static constexpr bool kcontig = LAYOUT == KC;
+  static constexpr int ROWS = kcontig ? MN : BK;                 // outer extent
+  static constexpr int INNER = kcontig ? BK : MN;                // inner extent (elements)
+  static constexpr int ROW_BYTES = 2 * INNER;
+  static constexpr int CPR = ROW_BYTES / 16;                     // 16-byte chunks per row
+  static constexpr int BYTES = ROWS * ROW_BYTES;
+  static constexpr int CHUNKS = BYTES / 16;
+  static constexpr int LOADS = CHUNKS / NT;                      // 16-byte loads per thread
+  static constexpr int ROW_STEP = NT / CPR;                      // rows between a thread's loads
+  static constexpr int SWZ_PERIOD = kcontig ? 16 : 4;            // rows after which the swizzle repeats
+  static_assert(CHUNKS % NT == 0, "tile must split evenly into 16-byte loads");
+  static_assert(NT % CPR == 0 && ROW_STEP % SWZ_PERIOD == 0,
+                "a thread's chunks must share one swizzle phase");
+};
+
+template <int IN>
+__device__ __forceinline__ v16f32 mfma_32x32x16(v8i16 a, v8i16 b, v16f32 c) {
+  if constexpr (IN == IN_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf16, a),
+                                                   __builtin_bit_cast(v8bf16, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8f16, a),
+                                                  __builtin_bit_cast(v8f16, b), c, 0, 0, 0);
+}
+
+// One 32x32x16 operand fragment: lane l gets row/column (l & 31) of the
+// fragment starting at `base`, k = 16*kk + 8*(l >> 5) + 0..7.
+template <class OT>
+__device__ __forceinline__ v8i16 read_frag(const char *lds, int lane, int base, int kk) {
+  if constexpr (OT::kcontig) {
+    return *(const v8i16 *)(lds + frag_kc_offset(lane, base, kk, OT::ROW_BYTES));
+  } else {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(lds + frag_tr_offset(lane, base, kk, 0, OT::ROW_BYTES)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(lds + frag_tr_offset(lane, base, kk, 1, OT::ROW_BYTES)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void *C, int64_t idx, float v) {
+  if constexpr (OUT == OUT_F32) {
+    ((float *)C)[idx] = v;
+  } else if constexpr (OUT == OUT_BF16) {
+    ((__bf16 *)C)[idx] = (__bf16)v;          // v_cvt_pk_bf16_f32: round to nearest even
+  } else {
+    ((_Float16 *)C)[idx] = (_Float16)v;      // v_cvt_f16_f32: round to nearest even
+  }
+}
+
+// Epilogue: accumulator register r of lane l holds row
+// 8*(r >> 2) + 4*(l >> 5) + (r & 3) and column (l & 31) of its 32x32 block
+// (layout checked with a probe).  Interior tiles store unmasked; edge tiles
+// mask rows >= M and columns >= N.
+template <class T, int OUT>
+__device__ __forceinline__ void epilogue(void *C, const v16f32 (&acc)[T::FM][T::FN], int M, int N,
+                                         int64_t ldc, int m0, int n0, int wm, int wn, int lane) {
+  const bool interior = M - m0 >= T::BM && N - n0 >= T::BN;
+  const int row0 = m0 + wm * T::TM + 4 * (lane >> 5);
+  const int col0 = n0 + wn * T::TN + (lane & 31);
+  if (interior) {
+#pragma unroll
+    for (int i = 0; i < T::FM; i++)
+#pragma unroll
+      for (int j = 0; j < T::FN; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          store_out<OUT>(C, (int64_t)(row0 + 32 * i + 8 * (r >> 2) + (r & 3)) * ldc + col0 + 32 * j,
+                         acc[i][j][r]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::FM; i++)
+#pragma unroll
+      for (int j = 0; j < T::FN; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
+          const int col = col0 + 32 * j;
+          if (row < M && col < N) store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][r]);
+        }
+  }
+}
+
+}  // namespace lsm

@@ -1,0 +1,248 @@
+// gemm_kernel_dma.h -- the LDS-staged GEMM kernel with direct global->LDS
+// loads, for gfx950.
+//
+// Operand tiles move from HBM straight into LDS with
+// `buffer_load_dwordx4 ... lds`: no VGPR staging and no ds_write.  This is the
+// asynchronous direct-to-LDS fill of "An educational GEMM ladder for Helios
+// GPUs", "Level 2: Asynchronous HBM Loads", on gfx950's LDS-DMA form of the
+// buffer load.  The hardware writes lane L's 16 bytes to LDS slot L of the
+// instruction's 1 KiB block (M0 holds the block address), which has two
+// consequences:
+//  * The XOR swizzle moves to the global side.  Lane L fills physical chunk
+//    p = L mod (chunks per row) of its row, so it loads logical chunk
+//    p XOR swizzle(row) from memory.  The LDS image is the same swizzled
+//    layout the register-staged kernel writes, and it is read back the same
+//    way.
+//  * Edges cost nothing.  The buffer descriptor's record count is the
+//    operand's exact footprint, so rows past the matrix read as zero.  Chunks
+//    past the contiguous extent get an offset beyond the record count and
+//    read as zero too.  Whole chunks only: the contiguous extents must be
+//    multiples of 8 elements, and the host sends other shapes to the
+//    register-staged kernel.
+//
+// The loads are issued with inline assembly.  The compiler's builtin form is
+// tracked by its wait-count pass, which cannot tell that the in-flight loads
+// target the other LDS stage and makes every ds_read_b64_tr_b16 wait for all
+// of them.  Here the kernel orders the loads itself:
+//   "s_waitcnt vmcnt(0)" + s_barrier publishes a stage before any wave
+//   reads it, and no load targets a stage until the barrier after the last
+//   read of that stage.
+//
+// Pipeline, two LDS stages (t = K tile, s = t & 1):
+//   for each k-step kk < last: read fragments of kk+1 (stage s) while the
+//                              MFMAs of kk run (register double buffer,
+//                              "Level 5: Deepening the K Stride");
+//   last k-step:  wait own loads, barrier (tile t+1 is in stage s^1 and
+//                 stage s is free), read fragments of kk=0 from stage s^1,
+//                 start the loads of tile t+2 into stage s, then run the
+//                 MFMAs of the last kk from registers.
+// The barrier therefore sits after the last LDS read of a stage and before
+// the last MFMAs that need no LDS ("Level 8: Using Split Barriers": signal
+// after the final LDS read, finish the register-only MFMAs, then continue).
+// Loads of tile t+2 have one K step (64 MFMAs per wave) to land.
+//
+// Wave tile 128 x 128 with 4 waves, one per SIMD: each k-step of 16 reads
+// 8 fragments (8 KiB) for 16 MFMAs, 2/3 of the LDS read traffic per flop of a
+// 128 x 64 wave tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+
+namespace lsm {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle, stride 0): byte offsets are range-checked against num_records.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+// An offset that is always past the record count (footprints stay below 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((a >> 32) & 0xFFFFu);   // base[47:32]; stride 0
+  r[2] = (int)bytes;                    // num_records
+  r[3] = (int)kBufferWord3;
+  return r;
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane L's bytes at
+// base + voff + soff land at LDS byte address lds_block + 16*L.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_block, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_block), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue this wave's loads of one operand tile.  Round i of the workgroup
+// covers chunk slots [i*NT, (i+1)*NT); this wave fills the 1 KiB block at
+// slot i*NT + 64*wave.
+template <class OT, int NT>
+__device__ __forceinline__ void dma_tile(i32x4 rs, uint32_t lds_tile, int wave, uint32_t voff,
+                                         uint32_t soff, uint32_t round_step) {
+#pragma unroll
+  for (int i = 0; i < OT::LOADS; i++)
+    dma16(rs, lds_tile + (uint32_t)((i * NT + 64 * wave) * 16), voff, soff + i * round_step);
+}
+
+// Byte offset, from the operand's base, of this thread's round-0 chunk in K
+// tile 0, or kOutOfRange when the chunk lies outside the matrix.
+//   K-contiguous:  row = M/N index (mn0 + row), inner = k
+//   MN-contiguous: row = k index, inner = M/N index (mn0 + inner)
+template <class OT>
+__device__ __forceinline__ uint32_t dma_lane_offset(int tid, int mn0, int mn_ext, int64_t ld,
+                                                    uint32_t bytes, int &inner_out) {
+  const int row = loader_row(tid, OT::ROW_BYTES);
+  const int pchunk = loader_chunk(tid, OT::ROW_BYTES);
+  const int lchunk = pchunk ^ (OT::kcontig ? kc_swizzle(row, OT::ROW_BYTES)
+                                           : mn_swizzle(row, OT::ROW_BYTES));
+  const int inner = 8 * lchunk;
+  inner_out = inner;
+  int64_t off;
+  if constexpr (OT::kcontig) {
+    off = ((int64_t)(mn0 + row) * ld + inner) * 2;
+  } else {
+    if (mn0 + inner >= mn_ext) return kOutOfRange;
+    off = ((int64_t)row * ld + mn0 + inner) * 2;
+  }
+  return off < (int64_t)bytes ? (uint32_t)off : kOutOfRange;
+}
+
+template <class T, class OA, class OB>
+struct Frags {
+  v8i16 a[T::FM], b[T::FN];
+};
+
+// Reads in the order the MFMAs (row-fragment major) consume them: a[0] with
+// every b[j] first, then the remaining a[i].
+template <class T, class OA, class OB>
+__device__ __forceinline__ void read_frags(Frags<T, OA, OB> &f, const char *sA, const char *sB,
+                                           int lane, int wm, int wn, int kk) {
+  f.a[0] = read_frag<OA>(sA, lane, wm * T::TM, kk);
+#pragma unroll
+  for (int j = 0; j < T::FN; j++) f.b[j] = read_frag<OB>(sB, lane, wn * T::TN + 32 * j, kk);
+#pragma unroll
+  for (int i = 1; i < T::FM; i++) f.a[i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+}
+
+template <class T, int IN, class OA, class OB>
+__device__ __forceinline__ void mfma_block(v16f32 (&acc)[T::FM][T::FN], const Frags<T, OA, OB> &f) {
+#pragma unroll
+  for (int i = 0; i < T::FM; i++)
+#pragma unroll
+    for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_32x32x16<IN>(f.a[i], f.b[j], acc[i][j]);
+}
+
+// Interleave the LDS reads of the next k-step with the MFMAs of this one:
+// one MFMA, then one ds_read, until the reads run out.
+template <int MFMAS, int READS>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+#pragma unroll
+  for (int q = 0; q < MFMAS; q++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+    if (q < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+  }
+}
+
+template <class T, int LA, int LB, int IN, int OUT>
+__global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
+    uint32_t a_bytes, uint32_t b_bytes) {
+  using OA = OperandTile<T::BM, T::BK, LA, T::NT>;
+  using OB = OperandTile<T::BN, T::BK, LB, T::NT>;
+  using F = Frags<T, OA, OB>;
+  static_assert(T::KSTEPS % 2 == 0, "the register double buffer alternates two k-steps");
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int READS = T::FM * (OA::kcontig ? 1 : 2) + T::FN * (OB::kcontig ? 1 : 2);
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WN, wn = wave % T::WN;
+
+  int tm, tn;
+  tile_coords(xcd_logical_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, T::GROUP_M, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+  const i32x4 rsA = buffer_rsrc(A, a_bytes);
+  const i32x4 rsB = buffer_rsrc(B, b_bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+
+  int a_inner, b_inner;
+  const uint32_t a_voff = dma_lane_offset<OA>(tid, m0, M, lda, a_bytes, a_inner);
+  const uint32_t b_voff = dma_lane_offset<OB>(tid, n0, N, ldb, b_bytes, b_inner);
+  // Advance per load round (ROW_STEP rows) and per K tile, in bytes.
+  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * 2);
+  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * 2);
+  const uint32_t a_kstep = (uint32_t)(LA == KC ? 2 * T::BK : 2 * T::BK * lda);
+  const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
+    const int k0 = kt * T::BK;
+    uint32_t av = a_voff, bv = b_voff;
+    if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
+      if constexpr (LA == KC) av = k0 + a_inner < K ? a_voff : kOutOfRange;
+      if constexpr (LB == KC) bv = k0 + b_inner < K ? b_voff : kOutOfRange;
+    }
+    dma_tile<OA, T::NT>(rsA, st, wave, av, (uint32_t)kt * a_kstep, a_round);
+    dma_tile<OB, T::NT>(rsB, st + OA::BYTES, wave, bv, (uint32_t)kt * b_kstep, b_round);
+  };
+
+  v16f32 acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; i++)
+#pragma unroll
+    for (int j = 0; j < T::FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  const int KT = (K + T::BK - 1) / T::BK;
+  F cur, nxt;
+  if (KT > 0) {
+    issue(0);
+    wait_dma();
+    __syncthreads();                       // tile 0 is in stage 0
+    if (KT > 1) issue(1);                  // tile 1 -> stage 1, lands during step 0
+    read_frags(cur, smem, smem + OA::BYTES, lane, wm, wn, 0);
+  }
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char *sA = smem + (kt & 1) * STAGE;
+    const char *sB = sA + OA::BYTES;
+#pragma unroll
+    for (int kk = 0; kk + 1 < T::KSTEPS; kk += 2) {
+      read_frags(nxt, sA, sB, lane, wm, wn, kk + 1);
+      mfma_block<T, IN>(acc, cur);
+      interleave_reads_with_mfma<T::FM * T::FN, READS>();
+      if (kk + 2 < T::KSTEPS) {
+        read_frags(cur, sA, sB, lane, wm, wn, kk + 2);
+        mfma_block<T, IN>(acc, nxt);
+        interleave_reads_with_mfma<T::FM * T::FN, READS>();
+      }
+    }
+    // `nxt` holds the last k-step of this stage (KSTEPS is even).
+    if (kt + 1 < KT) {
+      wait_dma();
+      __syncthreads();                     // tile kt+1 is in stage (kt+1)&1; stage kt&1 is free
+      const char *nA = smem + ((kt + 1) & 1) * STAGE;
+      read_frags(cur, nA, nA + OA::BYTES, lane, wm, wn, 0);
+      if (kt + 2 < KT) issue(kt + 2);
+    }
+    mfma_block<T, IN>(acc, nxt);
+  }
+
+  epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
+}
+
+}  // namespace lsm
