@@ -9,6 +9,7 @@
 
 #include "gemm_kernel.h"
 #include "gemm_kernel_dma.h"
+#include "gemm_kernel_pingpong.h"
 #include "lds_gemm.h"
 
 struct gemm_ctx {
@@ -33,6 +34,8 @@ using Skinny = Tile<32, 64, 64, 1, 2, 8>;
 //   DmaMid: 128 x 128 x 64, wave tile 64 x 64, LDS 2 x 32 KiB.
 using DmaBig = Tile<256, 256, 64, 2, 2, 8>;
 using DmaMid = Tile<128, 128, 64, 2, 2, 8>;
+// Ping-pong kernel: 256 x 256 x 64, 8 waves in two groups, wave tile 128 x 64.
+using PingPong = Tile<256, 256, 64, 2, 4, 8>;
 
 struct Args {
   const uint16_t *A;
@@ -43,7 +46,9 @@ struct Args {
   uint32_t a_bytes, b_bytes;   // operand footprints (used by the direct-to-LDS kernel)
 };
 
-template <class T, int LA, int LB, int IN, int OUT>
+enum Kind { REG = 0, DMA = 1, PINGPONG = 2 };
+
+template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   int tiles_m = (a.M + T::BM - 1) / T::BM;
   int tiles_n = (a.N + T::BN - 1) / T::BN;
@@ -53,8 +58,12 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
   uint32_t ab = a.a_bytes, bb = a.b_bytes;
   void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb};
-  return hipLaunchKernel((const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT>,
-                         dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
+  const void *fn;
+  if constexpr (KIND == PINGPONG)
+    fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT>;
+  else
+    fn = (const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT>;
+  return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
 }
 
 template <class T, int LA, int LB, int IN, int OUT>
@@ -70,15 +79,15 @@ static hipError_t launch(const Args &a, hipStream_t stream) {
                          dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
 }
 
-template <class T, bool DMA, int LA, int LB, int IN, int OUT>
+template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_kind(const Args &a, hipStream_t s) {
-  if constexpr (DMA)
-    return launch_dma<T, LA, LB, IN, OUT>(a, s);
-  else
+  if constexpr (KIND == REG)
     return launch<T, LA, LB, IN, OUT>(a, s);
+  else
+    return launch_dma<T, KIND, LA, LB, IN, OUT>(a, s);
 }
 
-template <class T, bool DMA, int IN, int OUT>
+template <class T, int DMA, int IN, int OUT>
 static hipError_t launch_layout(const Args &a, int la, int lb, hipStream_t s) {
   if (la == KC && lb == KC) return launch_kind<T, DMA, KC, KC, IN, OUT>(a, s);
   if (la == KC && lb == MNC) return launch_kind<T, DMA, KC, MNC, IN, OUT>(a, s);
@@ -86,7 +95,7 @@ static hipError_t launch_layout(const Args &a, int la, int lb, hipStream_t s) {
   return launch_kind<T, DMA, MNC, MNC, IN, OUT>(a, s);
 }
 
-template <class T, bool DMA = false>
+template <class T, int DMA = REG>
 static hipError_t launch_dtype(const Args &a, int la, int lb, int dtype, hipStream_t s) {
   switch (dtype) {
     case GEMM_BF16_F32: return launch_layout<T, DMA, IN_BF16, OUT_F32>(a, la, lb, s);
@@ -118,9 +127,9 @@ static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t
   if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
   const bool dma = dma_ok(a, la, lb);
   if (dma && ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256)
-    return launch_dtype<DmaBig, true>(a, la, lb, dtype, s);
+    return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
   if (dma && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64)
-    return launch_dtype<DmaMid, true>(a, la, lb, dtype, s);
+    return launch_dtype<DmaMid, DMA>(a, la, lb, dtype, s);
   if (ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256) return launch_dtype<Big>(a, la, lb, dtype, s);
   if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64) return launch_dtype<Mid>(a, la, lb, dtype, s);
   return launch_dtype<Small>(a, la, lb, dtype, s);

@@ -73,12 +73,18 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
 
 // One 16-byte-per-lane direct-to-LDS load: lane L's bytes at
 // base + voff + soff land at LDS byte address lds_block + 16*L.
+// The compiler reserves M0 and warns when asm clobbers it.  In these kernels
+// no compiler-generated instruction reads M0 (gfx950 LDS instructions do not
+// use it), and every asm statement sets M0 right before the load that uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_block, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_block), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -1,0 +1,168 @@
+// gemm_kernel_pingpong.h -- LDS-staged GEMM with direct-to-LDS loads and a
+// two-group ping-pong schedule, for gfx950.
+//
+// Eight waves, two per SIMD, in two groups of four (waves 0-3 and 4-7; wave
+// w runs on SIMD w mod 4).  Each wave owns a 128 x 64 block of the 256 x 256
+// workgroup tile.  The groups alternate between two kinds of phase,
+// separated by workgroup barriers:
+//   memory phase  M(t): read every MFMA fragment of K tile t from LDS into
+//                       registers (group 0 also starts the direct-to-LDS
+//                       loads of tile t+1);
+//   compute phase C(t): the 32 MFMAs of tile t, from registers only.
+// Group 1 starts one phase late, so while one wave of a SIMD issues MFMAs the
+// other wave of that SIMD moves data.  On gfx950 an MFMA stream and LDS->VGPR
+// returns overlap when they come from different waves of a SIMD, and mostly
+// serialize when one wave interleaves both (measured on MI355X with a
+// microbenchmark; the pages report the same scheduling family -- four-wave
+// interleave and eight- or sixteen-wave ping-pong -- working on MI355X,
+// "An educational GEMM ladder for Helios GPUs", Summary).
+//
+// Barrier b (0-based, all eight waves):
+//   b = 0          after the prologue loads of tiles 0 and 1 (tile 0 landed)
+//   group 0: M(t) ... b = 2t+1 ... C(t) ... b = 2t+2
+//   group 1: idle ... b = 1; then M(t) ... b = 2t+2 ... C(t) ... b = 2t+3
+// Group 1 skips the barrier after its last compute phase, so both groups
+// pass 2*KT + 1 barriers.
+// LDS hazards (tile t lives in stage t & 1):
+//  * stage t&1 is read between barriers 2t and 2t+2; the loads of tile t+2
+//    into it start after barrier 2t+2 (group 0, during M(t+1));
+//  * every wave waits for its own LDS reads before the barrier that ends its
+//    memory phase, and group 0 waits for its loads (vmcnt(0)) before the
+//    barrier that ends its compute phase, so tile t+1 is complete at barrier
+//    2t+2, before any wave reads it.
+// Loads of tile t+1 therefore have two phases (64 MFMAs per SIMD) to land.
+//
+// The LDS layout, the swizzle on the global side of the loads, the edge
+// handling through buffer range checks and the inline-assembly loads are
+// those of gemm_kernel_dma.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "gemm_kernel_dma.h"
+
+namespace lsm {
+
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Ping-pong tile: 256 x 256 x 64, waves 2 (M) x 4 (N), wave tile 128 x 64.
+template <class T, int LA, int LB, int IN, int OUT>
+__global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
+    uint32_t a_bytes, uint32_t b_bytes) {
+  static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
+  constexpr int LOADERS = T::NT / 2;                     // group 0 issues every load
+  using OA = OperandTile<T::BM, T::BK, LA, LOADERS>;
+  using OB = OperandTile<T::BN, T::BK, LB, LOADERS>;
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int LOADS_PER_TILE = OA::LOADS + OB::LOADS;  // per group-0 wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;                           // 0: waves 0-3, 1: waves 4-7
+  const int wm = group, wn = wave & 3;
+
+  int tm, tn;
+  tile_coords(xcd_logical_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, T::GROUP_M, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+
+  const i32x4 rsA = buffer_rsrc(A, a_bytes);
+  const i32x4 rsB = buffer_rsrc(B, b_bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+
+  // Loader geometry for group 0 (tid < LOADERS).
+  int a_inner, b_inner;
+  const uint32_t a_voff = dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, a_inner);
+  const uint32_t b_voff = dma_lane_offset<OB>(tid & (LOADERS - 1), n0, N, ldb, b_bytes, b_inner);
+  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * 2);
+  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * 2);
+  const uint32_t a_kstep = (uint32_t)(LA == KC ? 2 * T::BK : 2 * T::BK * lda);
+  const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
+  const int lwave = wave & 3;
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
+    const int k0 = kt * T::BK;
+    uint32_t av = a_voff, bv = b_voff;
+    if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
+      if constexpr (LA == KC) av = k0 + a_inner < K ? a_voff : kOutOfRange;
+      if constexpr (LB == KC) bv = k0 + b_inner < K ? b_voff : kOutOfRange;
+    }
+    dma_tile<OA, LOADERS>(rsA, st, lwave, av, (uint32_t)kt * a_kstep, a_round);
+    dma_tile<OB, LOADERS>(rsB, st + OA::BYTES, lwave, bv, (uint32_t)kt * b_kstep, b_round);
+  };
+
+  v16f32 acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; i++)
+#pragma unroll
+    for (int j = 0; j < T::FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+  const int KT = (K + T::BK - 1) / T::BK;
+  if (KT > 0) {
+    if (group == 0) {
+      issue(0);
+      if (KT > 1) {
+        issue(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_TILE) : "memory");   // tile 0 landed
+      } else {
+        wait_dma();
+      }
+    }
+    wg_barrier();                                        // b = 0
+    if (group == 1) wg_barrier();                        // b = 1: group 1 idles through M(0) of group 0
+
+    v8i16 fa[T::KSTEPS][T::FM], fb[T::KSTEPS][T::FN];
+    for (int kt = 0; kt < KT; ++kt) {
+      // ---- memory phase M(kt)
+      // The loads of tile kt+1 go first: their stage was freed at the last
+      // barrier and they have until the end of C(kt) to land.
+      if (group == 0 && kt >= 1 && kt + 1 < KT) issue(kt + 1);
+      const char *sA = smem + (kt & 1) * STAGE;
+      const char *sB = sA + OA::BYTES;
+#pragma unroll
+      for (int kk = 0; kk < T::KSTEPS; ++kk) {
+#pragma unroll
+        for (int i = 0; i < T::FM; i++) fa[kk][i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) fb[kk][j] = read_frag<OB>(sB, lane, wn * T::TN + 32 * j, kk);
+      }
+      wait_lds_reads();
+      wg_barrier();                                      // end of M(kt)
+
+      // ---- compute phase C(kt)
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < T::KSTEPS; ++kk)
+#pragma unroll
+        for (int i = 0; i < T::FM; i++)
+#pragma unroll
+          for (int j = 0; j < T::FN; j++)
+            acc[i][j] = mfma_32x32x16<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+      __builtin_amdgcn_s_setprio(0);
+      if (group == 0) {
+        wait_dma();                                      // tile kt+1 landed
+        wg_barrier();                                    // end of C(kt)
+      } else if (kt + 1 < KT) {
+        wg_barrier();
+      }
+    }
+  }
+
+  epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
+}
+
+}  // namespace lsm
