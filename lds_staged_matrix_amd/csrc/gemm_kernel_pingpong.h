@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "gemm_kernel_dma.h"
 
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   using OB = OperandTile<T::BN, T::BK, LB, LOADERS>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int LOADS_PER_TILE = OA::LOADS + OB::LOADS;  // per group-0 wave
+  constexpr int FRAGS = T::KSTEPS * (T::FM + T::FN);      // fragment reads per memory phase
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -91,16 +94,31 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
   const int lwave = wave & 3;
 
-  auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
+  // Byte offsets of this wave's loads of K tile kt (round i of A is load i,
+  // round i of B is load OA::LOADS + i).
+  auto voffs = [&](int kt, uint32_t &av, uint32_t &bv) {
     const int k0 = kt * T::BK;
-    uint32_t av = a_voff, bv = b_voff;
+    av = a_voff;
+    bv = b_voff;
     if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
       if constexpr (LA == KC) av = k0 + a_inner < K ? a_voff : kOutOfRange;
       if constexpr (LB == KC) bv = k0 + b_inner < K ? b_voff : kOutOfRange;
     }
-    dma_tile<OA, LOADERS>(rsA, st, lwave, av, (uint32_t)kt * a_kstep, a_round);
-    dma_tile<OB, LOADERS>(rsB, st + OA::BYTES, lwave, bv, (uint32_t)kt * b_kstep, b_round);
+  };
+  auto issue_one = [&](int kt, int d, uint32_t av, uint32_t bv) {
+    const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
+    if (d < OA::LOADS)
+      dma16(rsA, st + (uint32_t)((d * LOADERS + 64 * lwave) * 16), av,
+            (uint32_t)kt * a_kstep + d * a_round);
+    else
+      dma16(rsB, st + OA::BYTES + (uint32_t)(((d - OA::LOADS) * LOADERS + 64 * lwave) * 16), bv,
+            (uint32_t)kt * b_kstep + (d - OA::LOADS) * b_round);
+  };
+  auto issue = [&](int kt) {
+    uint32_t av, bv;
+    voffs(kt, av, bv);
+#pragma unroll
+    for (int d = 0; d < LOADS_PER_TILE; d++) issue_one(kt, d, av, bv);
   };
 
   v16f32 acc[T::FM][T::FN];
@@ -128,18 +146,39 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     v8i16 fa[T::KSTEPS][T::FM], fb[T::KSTEPS][T::FN];
     for (int kt = 0; kt < KT; ++kt) {
       // ---- memory phase M(kt)
-      // The loads of tile kt+1 go first: their stage was freed at the last
-      // barrier and they have until the end of C(kt) to land.
-      if (group == 0 && kt >= 1 && kt + 1 < KT) issue(kt + 1);
+      // Group 0 also starts the loads of tile kt+1 (their stage was freed at
+      // the last barrier; they have until the end of C(kt) to land).  The
+      // load issue blocks while the CU's load queue drains, so it is
+      // interleaved with the fragment reads, whose issue blocks on a
+      // different counter: two loads after each of the first frag reads.
       const char *sA = smem + (kt & 1) * STAGE;
       const char *sB = sA + OA::BYTES;
+      auto m_phase = [&](auto with_loads) {
+        constexpr bool LOAD = decltype(with_loads)::value;
+        uint32_t av = 0, bv = 0;
+        if constexpr (LOAD) voffs(kt + 1, av, bv);
 #pragma unroll
-      for (int kk = 0; kk < T::KSTEPS; ++kk) {
+        for (int kk = 0; kk < T::KSTEPS; ++kk) {
 #pragma unroll
-        for (int i = 0; i < T::FM; i++) fa[kk][i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+          for (int i = 0; i < T::FM + T::FN; i++) {
+            if (i < T::FM)
+              fa[kk][i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+            else
+              fb[kk][i - T::FM] = read_frag<OB>(sB, lane, wn * T::TN + 32 * (i - T::FM), kk);
+            if constexpr (LOAD) {
+              // spread LOADS_PER_TILE loads evenly over the FRAGS fragment reads
+              const int q = kk * (T::FM + T::FN) + i;
 #pragma unroll
-        for (int j = 0; j < T::FN; j++) fb[kk][j] = read_frag<OB>(sB, lane, wn * T::TN + 32 * j, kk);
-      }
+              for (int d = q * LOADS_PER_TILE / FRAGS; d < (q + 1) * LOADS_PER_TILE / FRAGS; d++)
+                issue_one(kt + 1, d, av, bv);
+            }
+          }
+        }
+      };
+      if (group == 0 && kt >= 1 && kt + 1 < KT)
+        m_phase(std::true_type{});
+      else
+        m_phase(std::false_type{});
       wait_lds_reads();
       wg_barrier();                                      // end of M(kt)
 
