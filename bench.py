@@ -30,9 +30,7 @@ METRIC = "bf16 GEMM TFLOP/s + % of MFMA peak; LDS bank-conflict rate (1 MI355X)"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 2516.6
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_nn_f32"
-KERNEL_SOURCES = ["lds_staged_matrix_amd/csrc/gemm_kernel.h",
-                  "lds_staged_matrix_amd/csrc/lds_layout.h",
-                  "lds_staged_matrix_amd/csrc/gemm_api.hip"]
+KERNEL_DIR = "lds_staged_matrix_amd/csrc"
 DTYPE_CODE = {("bf16", "f32"): 0, ("bf16", "bf16"): 1, ("f16", "f16"): 2, ("f16", "f32"): 3}
 
 
@@ -42,9 +40,12 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    d = os.path.join(ROOT, KERNEL_DIR)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -96,12 +97,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layout", default=None, help="e.g. K,MN (A contiguity, B contiguity)")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="rows of C the oracle computes for the CPU baseline "
+                         "(default: about 6e10 flops' worth, 10-20 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--flushed", action="store_true",
-                    help="also time 20 launches with a 1 GiB cache flush before each")
+                    help="also time 20 launches with the caches flushed before each "
+                         "(always done for HBM-bound workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -167,12 +171,20 @@ def main():
     wall = time.perf_counter() - t0
     kern_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
-    # Same kernel with the caches flushed before each launch (the pages'
-    # method), timed per launch outside the flush.
+    flops = 2.0 * M * N * K
+    out_bytes = 4 if w["out"] == "f32" else 2
+    alg_bytes = 2.0 * (M * K + K * N) + out_bytes * M * N
+    hbm_bound = flops / alg_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+
+    # Same kernel with cold caches (the pages' method): before each launch,
+    # outside its events, read 1 GiB so that L2 and the 256 MB Infinity Cache
+    # hold none of A, B or C.  The flush reads (a write would leave dirty
+    # lines whose write-back competes with the timed kernel).
     fl_ms = []
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flushed else None
-    for i in range(20 if args.flushed else 0):
-        flush.fill_(i & 0xFF)
+    do_flush = args.flushed or hbm_bound
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if do_flush else None
+    for i in range(20 if do_flush else 0):
+        flush.sum()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
         step()
@@ -180,14 +192,9 @@ def main():
         torch.cuda.synchronize()
         fl_ms.append(s.elapsed_time(e))
     del flush
-
-    flops = 2.0 * M * N * K
-    out_bytes = 4 if w["out"] == "f32" else 2
-    alg_bytes = 2.0 * (M * K + K * N) + out_bytes * M * N
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     kavg = float(kern_ms.mean())
-    hbm_bound = flops / alg_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
     if hbm_bound:
         achieved = alg_bytes / (kavg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -209,7 +216,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        rows = max(1, min(args.cpu_rows, M))
+        rows = args.cpu_rows if args.cpu_rows else int(6e10 / (2.0 * N * K))
+        rows = max(1, min(rows, M))
         cpu = cpu_baseline(p, rows)
         log(f"cpu baseline: {cpu}")
 

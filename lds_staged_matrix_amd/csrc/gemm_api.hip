@@ -10,6 +10,7 @@
 #include "gemm_kernel.h"
 #include "gemm_kernel_dma.h"
 #include "gemm_kernel_pingpong.h"
+#include "gemm_kernel_skinny.h"
 #include "lds_gemm.h"
 
 struct gemm_ctx {
@@ -36,6 +37,9 @@ using DmaBig = Tile<256, 256, 64, 2, 2, 8>;
 using DmaMid = Tile<128, 128, 64, 2, 2, 8>;
 // Ping-pong kernel: 256 x 256 x 64, 8 waves in two groups, wave tile 128 x 64.
 using PingPong = Tile<256, 256, 64, 2, 4, 8>;
+// Skinny kernel (M <= 32): 32 x 64 column slabs, K stages of 128, a ring of
+// 6 stages (144 KiB), 4 waves splitting each stage's K range.
+using SkinnyStream = SkinnyTile<64, 6>;
 
 struct Args {
   const uint16_t *A;
@@ -46,7 +50,7 @@ struct Args {
   uint32_t a_bytes, b_bytes;   // operand footprints (used by the direct-to-LDS kernel)
 };
 
-enum Kind { REG = 0, DMA = 1, PINGPONG = 2 };
+enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3 };
 
 template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_dma(const Args &a, hipStream_t stream) {
@@ -67,6 +71,18 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
 }
 
 template <class T, int LA, int LB, int IN, int OUT>
+static hipError_t launch_skinny(const Args &a, hipStream_t stream) {
+  const uint16_t *A = a.A, *B = a.B;
+  void *C = a.C;
+  int M = a.M, N = a.N, K = a.K;
+  int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
+  uint32_t ab = a.a_bytes, bb = a.b_bytes;
+  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &ab, &bb};
+  return hipLaunchKernel((const void *)lds_gemm_skinny_kernel<T, LA, LB, IN, OUT>,
+                         dim3((unsigned)((a.N + T::BN - 1) / T::BN)), dim3(T::NT), params, 0, stream);
+}
+
+template <class T, int LA, int LB, int IN, int OUT>
 static hipError_t launch(const Args &a, hipStream_t stream) {
   int tiles_m = (a.M + T::BM - 1) / T::BM;
   int tiles_n = (a.N + T::BN - 1) / T::BN;
@@ -83,6 +99,8 @@ template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_kind(const Args &a, hipStream_t s) {
   if constexpr (KIND == REG)
     return launch<T, LA, LB, IN, OUT>(a, s);
+  else if constexpr (KIND == SKINNY)
+    return launch_skinny<T, LA, LB, IN, OUT>(a, s);
   else
     return launch_dma<T, KIND, LA, LB, IN, OUT>(a, s);
 }
@@ -124,8 +142,9 @@ static bool dma_ok(const Args &a, int la, int lb) {
 // CUs work, else the 64 tile; M <= 32 takes the skinny tile.  Big and mid
 // shapes take the direct-to-LDS kernel when dma_ok() holds.
 static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t s) {
-  if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
   const bool dma = dma_ok(a, la, lb);
+  if (a.M <= 32 && dma) return launch_dtype<SkinnyStream, SKINNY>(a, la, lb, dtype, s);
+  if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
   if (dma && ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256)
     return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
   if (dma && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64)

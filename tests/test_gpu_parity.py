@@ -205,6 +205,35 @@ def test_config_8192_integer_exact():
     sample_check(p, C, lsm.GEMM_BF16_F32, True, [(0, 1), (4100, 4101), (8191, 8192)], 2000)
 
 
+# M <= 32 with whole 16-byte chunks along every contiguous extent: the
+# streaming skinny kernel (deep direct-to-LDS ring, K split over the waves,
+# partial sums reduced in LDS).  Partial last K stage, K shorter than the
+# ring, ragged N, odd M where A is K-contiguous.
+SKINNY_DMA = [(8, 136, 264), (32, 1000, 1032), (24, 4160, 520), (16, 64, 8), (32, 8, 128),
+              (8, 200, 3208)]
+SKINNY_DMA_KA = [(1, 520, 1000), (31, 264, 136), (17, 72, 2056)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_DMA)
+@pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
+def test_skinny_stream_integer_exact(shape, la, lb):
+    M, N, K = shape
+    check_full(M, N, K, la, lb, lsm.GEMM_BF16_F32, "int", (91, 92), ldc_pad=3, extra_rows=2)
+
+
+@pytest.mark.parametrize("shape", SKINNY_DMA_KA)
+@pytest.mark.parametrize("lb", ["MN", "K"])
+def test_skinny_stream_odd_m_integer_exact(shape, lb):
+    M, N, K = shape
+    check_full(M, N, K, "K", lb, lsm.GEMM_BF16_F32, "int", (93, 94), ldc_pad=1, extra_rows=1)
+
+
+@pytest.mark.parametrize("gdtype", ALL_DTYPES)
+@pytest.mark.parametrize("la,lb", [("K", "MN"), ("MN", "K")])
+def test_skinny_stream_real_all_dtypes(gdtype, la, lb):
+    check_full(24, 1160, 1544, la, lb, gdtype, "normal", (95, 96), ldc_pad=5, extra_rows=1)
+
+
 def test_config_skinny_bf16_out():
     w = synth.WORKLOADS["bf16_skinny_32x16384x8192_nn_bf16"]
     announce("skinny")
