@@ -31,15 +31,15 @@ using Mid = Tile<128, 128, 64, 2, 2, 8>;
 using Small = Tile<64, 64, 64, 2, 2, 4>;
 using Skinny = Tile<32, 64, 64, 1, 2, 8>;
 // Direct-to-LDS kernel shapes: 4 waves (one per SIMD).
-//   DmaBig: 256 x 256 x 64, wave tile 128 x 128, LDS 2 x 64 KiB.
 //   DmaMid: 128 x 128 x 64, wave tile 64 x 64, LDS 2 x 32 KiB.
-using DmaBig = Tile<256, 256, 64, 2, 2, 8>;
 using DmaMid = Tile<128, 128, 64, 2, 2, 8>;
+//   DmaSmall: 64 x 64 x 64, wave tile 32 x 32, LDS 2 x 16 KiB.
+using DmaSmall = Tile<64, 64, 64, 2, 2, 8>;
 // Ping-pong kernel: 256 x 256 x 64, 8 waves in two groups, wave tile 128 x 64.
 using PingPong = Tile<256, 256, 64, 2, 4, 8>;
-// Skinny kernel (M <= 32): 32 x 64 column slabs, K stages of 128, a ring of
-// 6 stages (144 KiB), 4 waves splitting each stage's K range.
-using SkinnyStream = SkinnyTile<64, 6>;
+// Split-K ring kernel, M <= 32: 32 x 64 column slabs, K stages of 128, a
+// ring of 6 stages (144 KiB), 4 waves splitting each stage's K range.
+using SkinnyStream = SkinnyTile<32, 64, 128, 6>;
 
 struct Args {
   const uint16_t *A;
@@ -72,14 +72,16 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
 
 template <class T, int LA, int LB, int IN, int OUT>
 static hipError_t launch_skinny(const Args &a, hipStream_t stream) {
+  int tiles_m = (a.M + T::BM - 1) / T::BM;
+  int tiles_n = (a.N + T::BN - 1) / T::BN;
   const uint16_t *A = a.A, *B = a.B;
   void *C = a.C;
   int M = a.M, N = a.N, K = a.K;
   int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
   uint32_t ab = a.a_bytes, bb = a.b_bytes;
-  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &ab, &bb};
+  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb};
   return hipLaunchKernel((const void *)lds_gemm_skinny_kernel<T, LA, LB, IN, OUT>,
-                         dim3((unsigned)((a.N + T::BN - 1) / T::BN)), dim3(T::NT), params, 0, stream);
+                         dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
 }
 
 template <class T, int LA, int LB, int IN, int OUT>
@@ -137,20 +139,25 @@ static bool dma_ok(const Args &a, int la, int lb) {
          (b_outer + 512) * a.ldb * 2 + 2 * (int64_t)a.K < lim;
 }
 
-// Shape classes.  The big tile when it still gives every CU at least one
-// workgroup, else the 128 tile when that gives at least a quarter of the
-// CUs work, else the 64 tile; M <= 32 takes the skinny tile.  Big and mid
-// shapes take the direct-to-LDS kernel when dma_ok() holds.
+// Shape classes.  M <= 32 takes the split-K ring kernel (HBM-bound).
+// Otherwise the big tile when it still gives every CU at least one
+// workgroup, else the 128 tile when that does, else the 64 tile (a short,
+// latency-bound K loop per workgroup; more workgroups hide more of it).
+// Shapes whose contiguous extents are not whole 16-byte chunks (dma_ok()
+// false) take the register-staged kernel of the same class.
 static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t s) {
   const bool dma = dma_ok(a, la, lb);
-  if (a.M <= 32 && dma) return launch_dtype<SkinnyStream, SKINNY>(a, la, lb, dtype, s);
+  const int64_t t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
+  const int64_t t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
+  if (dma) {
+    if (a.M <= 32) return launch_dtype<SkinnyStream, SKINNY>(a, la, lb, dtype, s);
+    if (t256 >= 256) return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
+    if (t128 >= 256) return launch_dtype<DmaMid, DMA>(a, la, lb, dtype, s);
+    return launch_dtype<DmaSmall, DMA>(a, la, lb, dtype, s);
+  }
   if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);
-  if (dma && ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256)
-    return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
-  if (dma && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64)
-    return launch_dtype<DmaMid, DMA>(a, la, lb, dtype, s);
-  if (ceil_div(a.M, 256) * ceil_div(a.N, 256) >= 256) return launch_dtype<Big>(a, la, lb, dtype, s);
-  if (ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 64) return launch_dtype<Mid>(a, la, lb, dtype, s);
+  if (t256 >= 256) return launch_dtype<Big>(a, la, lb, dtype, s);
+  if (t128 >= 64) return launch_dtype<Mid>(a, la, lb, dtype, s);
   return launch_dtype<Small>(a, la, lb, dtype, s);
 }
 
