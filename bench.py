@@ -9,6 +9,7 @@ Prints ONE JSON line on stdout.  Extra per-run detail goes to stderr.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
   python bench.py --profile-run      # a few launches only, for rocprofv3
   python bench.py --copy-calibration # one plain 1 GiB device copy, for rocprofv3 --pmc
+  python bench.py --variant noswizzle # an A/B build with one design choice changed
 """
 import argparse
 import hashlib
@@ -63,6 +64,21 @@ def read_traffic(workload, src_hash):
     return float(m_bytes.group(1))
 
 
+def read_conflict_rate(workload, layout_name, src_hash):
+    """LDS bank-conflict rate (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE) of
+    this workload from the committed rocprofv3 counter summary, or None when
+    there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "lds_bank_conflicts_all_workloads.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    m = re.search(rf"^rate {re.escape(workload)} {layout_name}:\s*([0-9.eE+-]+)", text, re.M)
+    if not m_hash or not m or m_hash.group(1) != src_hash:
+        return None
+    return float(m.group(1))
+
+
 def make_inputs(w, layout):
     import torch
     la, lb = layout
@@ -103,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--variant", default=None,
+                    help="benchmark an A/B build that changes one design choice "
+                         "(noswizzle, scalar_tr, ring2) instead of the library")
     ap.add_argument("--flushed", action="store_true",
                     help="also time 20 launches with the caches flushed before each "
                          "(always done for HBM-bound workloads)")
@@ -136,13 +155,14 @@ def main():
     p, A, B = make_inputs(w, layout)
     C = torch.empty(M * N, dtype=torch.float32 if w["out"] == "f32" else torch.int16,
                     device="cuda")
-    h = lsm.gemm_create()
+    lib = lsm.ablation_library(args.variant) if args.variant else lsm
+    h = lib.gemm_create()
     stream = torch.cuda.current_stream()
     la = lsm.GEMM_K_CONTIG if layout[0] == "K" else lsm.GEMM_MN_CONTIG
     lb = lsm.GEMM_K_CONTIG if layout[1] == "K" else lsm.GEMM_MN_CONTIG
 
     def step():
-        st = lsm.gemm_run(h, A, B, C, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream)
+        st = lib.gemm_run(h, A, B, C, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream)
         if st != lsm.GEMM_OK:
             raise lsm.GemmError(st, "gemm_run")
 
@@ -240,7 +260,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    lsm.gemm_destroy(h)
+    line["config"]["lds_bank_conflict_rate"] = None if args.variant else \
+        read_conflict_rate(args.workload, line["config"]["layout"], src_hash)
+    if args.variant:
+        line["config"]["ablation_build"] = args.variant
+        roof["traffic"] = None
+    lib.gemm_destroy(h)
     print(json.dumps(line), flush=True)
 
 

@@ -17,7 +17,8 @@ __all__ = [
     "GEMM_BF16_F32", "GEMM_BF16_BF16", "GEMM_F16_F16", "GEMM_F16_F32",
     "GEMM_OK", "GEMM_ERR_INVALID_ARG", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_DEVICE",
     "GEMM_ERR_LAUNCH", "GemmError", "library_path", "load_library", "gemm_create",
-    "gemm_run", "gemm_destroy", "gemm_status_str", "EXPORTED_SYMBOLS",
+    "gemm_run", "gemm_destroy", "gemm_status_str", "EXPORTED_SYMBOLS", "Library",
+    "ablation_library",
 ]
 
 GEMM_K_CONTIG, GEMM_MN_CONTIG = 0, 1
@@ -40,12 +41,7 @@ def library_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
 
-def load_library():
-    """Load liblds_gemm.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    path = library_path()
+def _open(path):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with lds_staged_matrix_amd/build.py "
                            "(or __graft_entry__.build()); there is no fallback path")
@@ -59,8 +55,15 @@ def load_library():
     lib.gemm_destroy.restype = i32
     lib.gemm_status_str.argtypes = [i32]
     lib.gemm_status_str.restype = ctypes.c_char_p
-    _lib = lib
     return lib
+
+
+def load_library():
+    """Load liblds_gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        _lib = _open(library_path())
+    return _lib
 
 
 def _ptr(x):
@@ -100,3 +103,40 @@ def gemm_destroy(h) -> int:
 
 def gemm_status_str(status: int) -> str:
     return load_library().gemm_status_str(status).decode()
+
+
+class Library:
+    """The same four entry points bound to one specific build of the library
+    (the default build, or an A/B build from ablation_library())."""
+
+    def __init__(self, path):
+        self.path = path
+        self._lib = _open(path)
+
+    def gemm_create(self):
+        h = ctypes.c_void_p()
+        st = self._lib.gemm_create(ctypes.byref(h))
+        if st != GEMM_OK:
+            raise GemmError(st, "gemm_create")
+        return h
+
+    def gemm_run(self, h, A, B, C, M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype,
+                 stream=None) -> int:
+        return self._lib.gemm_run(h, _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                  layoutA, layoutB, dtype, _stream(stream))
+
+    def gemm_destroy(self, h) -> int:
+        return self._lib.gemm_destroy(h)
+
+    def gemm_status_str(self, status: int) -> str:
+        return self._lib.gemm_status_str(status).decode()
+
+
+def ablation_library(name: str) -> Library:
+    """An A/B build of the library that changes one design choice (names in
+    build.VARIANTS); built by build.build_all().  Only benchmarks and tests
+    use these."""
+    from . import build as _build
+    if name not in _build.VARIANTS:
+        raise ValueError(f"unknown ablation build {name!r}; known: {sorted(_build.VARIANTS)}")
+    return Library(_build.variant_path(name))

@@ -1,4 +1,12 @@
-"""Build the HIP library liblds_gemm.so in-tree with hipcc for gfx950."""
+"""Build the HIP library liblds_gemm.so in-tree with hipcc for gfx950.
+
+Also builds, from the same sources:
+  * ablation/liblds_gemm_<name>.so -- the A/B builds that each change one
+    design choice (see VARIANTS), used by the benchmark and the counter runs
+    that measure what each choice buys;
+  * liblds_layout_host.so (and _noswizzle) -- host-only builds of the LDS
+    address functions, evaluated by the bank-conflict model in the tests.
+"""
 import os
 import subprocess
 
@@ -6,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblds_gemm.so")
+ABLATION_DIR = os.path.join(PKG, "ablation")
 SOURCES = ["gemm_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
@@ -13,10 +22,25 @@ FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
+# One design choice changed per build; the library itself uses none of these.
+VARIANTS = {
+    "noswizzle": ["-DLSM_LDS_SWIZZLE=0"],   # row-major LDS tiles, no XOR swizzle
+    "scalar_tr": ["-DLSM_TR_READ=0"],       # 8 x 16-bit LDS reads instead of ds_read_b64_tr_b16
+    "ring2": ["-DLSM_RING_STAGES=2"],       # M <= 32 kernel with a 2-stage instead of 6-stage ring
+}
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-shared",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(ABLATION_DIR, f"liblds_gemm_{name}.so")
+
+
+def layout_host_path(suffix: str = "") -> str:
+    return os.path.join(PKG, f"liblds_layout_host{suffix}.so")
+
+
+def _run(cmd, out, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -26,9 +50,43 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose: bool = False, extra_flags=(), variant: str = None) -> str:
+    """Build the library (or, with `variant`, one ablation build)."""
+    out = LIB
+    flags = list(extra_flags)
+    if variant is not None:
+        os.makedirs(ABLATION_DIR, exist_ok=True)
+        out = variant_path(variant)
+        flags = VARIANTS[variant] + flags
+    cmd = [HIPCC, *FLAGS, *flags, "-shared",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out + ".tmp"]
+    return _run(cmd, out, verbose)
+
+
+def build_layout_host(verbose: bool = False):
+    """Host-only builds of the LDS address functions (no device code)."""
+    outs = []
+    for suffix, flags in LAYOUT_HOST.items():
+        out = layout_host_path(suffix)
+        cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-shared", "-x", "hip", "--offload-host-only",
+               "-I", CSRC, *flags, os.path.join(CSRC, "layout_probe.cpp"), "-o", out + ".tmp"]
+        outs.append(_run(cmd, out, verbose))
+    return outs
+
+
+def build_all(verbose: bool = False):
+    """Every build, four hipcc processes at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [lambda: build(verbose)] + [lambda n=n: build(verbose, variant=n) for n in VARIANTS] + \
+           [lambda: build_layout_host(verbose)]
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        for f in [pool.submit(j) for j in jobs]:
+            f.result()
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build_all(verbose=True)

@@ -39,7 +39,12 @@ using DmaSmall = Tile<64, 64, 64, 2, 2, 8>;
 using PingPong = Tile<256, 256, 64, 2, 4, 8>;
 // Split-K ring kernel, M <= 32: 32 x 64 column slabs, K stages of 128, a
 // ring of 6 stages (144 KiB), 4 waves splitting each stage's K range.
-using SkinnyStream = SkinnyTile<32, 64, 128, 6>;
+// LSM_RING_STAGES overrides the ring depth only for the A/B build that
+// measures what the depth buys; the library is built with 6.
+#ifndef LSM_RING_STAGES
+#define LSM_RING_STAGES 6
+#endif
+using SkinnyStream = SkinnyTile<32, 64, 128, LSM_RING_STAGES>;
 
 struct Args {
   const uint16_t *A;

@@ -7,6 +7,14 @@
 
 #include "lds_layout.h"
 
+// LSM_TR_READ = 0 builds the kernels with the MN-contiguous operand read by
+// eight 16-bit LDS loads per fragment instead of two ds_read_b64_tr_b16; it
+// exists only for the A/B build that measures what the transposed read buys.
+// The library is built with the default, 1.
+#ifndef LSM_TR_READ
+#define LSM_TR_READ 1
+#endif
+
 namespace lsm {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -73,6 +81,15 @@ template <class OT>
 __device__ __forceinline__ v8i16 read_frag(const char *lds, int lane, int base, int kk) {
   if constexpr (OT::kcontig) {
     return *(const v8i16 *)(lds + frag_kc_offset(lane, base, kk, OT::ROW_BYTES));
+  } else if constexpr (!LSM_TR_READ) {
+    // element i of lane l: column base + (l & 31), k-row 16*kk + 8*(l >> 5) + i
+    const int col = base + (lane & 31);
+    v8i16 f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      f[i] = *(const short *)(lds + mn_chunk_offset(16 * kk + 8 * (lane >> 5) + i, col / 8,
+                                                    OT::ROW_BYTES) + 2 * (col & 7));
+    return f;
   } else {
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4i16 *)(lds + frag_tr_offset(lane, base, kk, 0, OT::ROW_BYTES)));

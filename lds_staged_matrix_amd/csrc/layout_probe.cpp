@@ -1,0 +1,24 @@
+// layout_probe.cpp -- host-callable views of the LDS address functions of
+// lds_layout.h, built host-only into a small shared library so that the
+// bank-conflict model in the tests evaluates exactly the addresses the
+// kernels use.  Nothing here runs on the GPU.
+#include "lds_layout.h"
+
+extern "C" {
+int lsm_layout_swizzled() { return LSM_LDS_SWIZZLE; }
+int lsm_kc_chunk_offset(int row, int chunk, int row_bytes) {
+  return lsm::kc_chunk_offset(row, chunk, row_bytes);
+}
+int lsm_mn_chunk_offset(int k, int chunk, int row_bytes) {
+  return lsm::mn_chunk_offset(k, chunk, row_bytes);
+}
+int lsm_loader_lds_offset(int id, int row_bytes, int k_contig) {
+  return lsm::loader_lds_offset(id, row_bytes, k_contig != 0);
+}
+int lsm_frag_kc_offset(int lane, int base, int kk, int row_bytes) {
+  return lsm::frag_kc_offset(lane, base, kk, row_bytes);
+}
+int lsm_frag_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
+  return lsm::frag_tr_offset(lane, base, kk, h, row_bytes);
+}
+}

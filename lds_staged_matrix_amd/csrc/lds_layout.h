@@ -42,6 +42,13 @@
 
 #include <hip/hip_runtime.h>
 
+// LSM_LDS_SWIZZLE = 0 builds the same kernels with unswizzled (row-major)
+// LDS tiles; it exists only for the A/B build that measures what the
+// swizzle buys.  The library is built with the default, 1.
+#ifndef LSM_LDS_SWIZZLE
+#define LSM_LDS_SWIZZLE 1
+#endif
+
 namespace lsm {
 
 // ---------------------------------------------------------------- swizzles
@@ -49,15 +56,18 @@ namespace lsm {
 // XOR applied to the chunk index of row `row` of a K-contiguous tile.
 __host__ __device__ constexpr int kc_swizzle(int row, int row_bytes) {
   // rows per 256-byte bank line and chunks per row
-  return row_bytes >= 256 ? (row & 15)
-                          : ((row / (256 / row_bytes)) & (row_bytes / 16 - 1));
+  return !LSM_LDS_SWIZZLE ? 0
+         : row_bytes >= 256 ? (row & 15)
+                            : ((row / (256 / row_bytes)) & (row_bytes / 16 - 1));
 }
 
 // XOR applied to the chunk index of k-row `k` of an MN-contiguous tile: the
 // four k rows read by one 32-lane transposed-read phase land in four distinct
 // 64-byte quarters of the bank line.
 __host__ __device__ constexpr int mn_swizzle(int k, int row_bytes) {
-  return row_bytes >= 256 ? 4 * (k & 3) : (row_bytes == 128 ? 4 * ((k >> 1) & 1) : 0);
+  return !LSM_LDS_SWIZZLE ? 0
+         : row_bytes >= 256 ? 4 * (k & 3)
+                            : (row_bytes == 128 ? 4 * ((k >> 1) & 1) : 0);
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
