@@ -66,7 +66,10 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   int M = a.M, N = a.N, K = a.K;
   int64_t lda = a.lda, ldb = a.ldb, ldc = a.ldc;
   uint32_t ab = a.a_bytes, bb = a.b_bytes;
-  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb};
+  // 16-byte C stores (LDS-staged epilogue) need C and every row start aligned
+  constexpr int64_t esz = OUT == OUT_F32 ? 4 : 2;
+  int c_vec = ((uintptr_t)C % 16 == 0) && ((ldc * esz) % 16 == 0);
+  void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb, &c_vec};
   const void *fn;
   if constexpr (KIND == PINGPONG)
     fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT>;

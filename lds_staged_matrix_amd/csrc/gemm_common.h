@@ -99,16 +99,29 @@ __device__ __forceinline__ v8i16 read_frag(const char *lds, int lane, int base, 
   }
 }
 
+// C is written with non-temporal stores: nothing in the kernel reads it back,
+// and on MI355X streaming it past the caches gave the fp32 8192^3 case 3-5%.
 template <int OUT>
 __device__ __forceinline__ void store_out(void *C, int64_t idx, float v) {
   if constexpr (OUT == OUT_F32) {
-    ((float *)C)[idx] = v;
+    __builtin_nontemporal_store(v, (float *)C + idx);
   } else if constexpr (OUT == OUT_BF16) {
-    ((__bf16 *)C)[idx] = (__bf16)v;          // v_cvt_pk_bf16_f32: round to nearest even
+    // v_cvt_pk_bf16_f32: round to nearest even
+    __builtin_nontemporal_store((__bf16)v, (__bf16 *)C + idx);
   } else {
-    ((_Float16 *)C)[idx] = (_Float16)v;      // v_cvt_f16_f32: round to nearest even
+    // v_cvt_f16_f32: round to nearest even
+    __builtin_nontemporal_store((_Float16)v, (_Float16 *)C + idx);
   }
 }
+
+template <int OUT>
+struct OutElem;
+template <>
+struct OutElem<OUT_F32> { typedef float type; };
+template <>
+struct OutElem<OUT_BF16> { typedef __bf16 type; };
+template <>
+struct OutElem<OUT_F16> { typedef _Float16 type; };
 
 // Epilogue: accumulator register r of lane l holds row
 // 8*(r >> 2) + 4*(l >> 5) + (r & 3) and column (l & 31) of its 32x32 block
@@ -140,6 +153,78 @@ __device__ __forceinline__ void epilogue(void *C, const v16f32 (&acc)[T::FM][T::
           const int col = col0 + 32 * j;
           if (row < M && col < N) store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][r]);
         }
+  }
+}
+
+// LDS-staged epilogue ("An educational GEMM ladder for Helios GPUs",
+// "Level 10"): each wave converts its accumulators to the output type into a
+// private LDS region laid out row-major, then reads it back 16 bytes per lane
+// and stores whole 16-byte pieces of C rows, so every store instruction
+// covers full 128-byte lines (4 rows of 64 fp32, 8 rows of 64 bf16/fp16)
+// instead of 32-lane half rows.  Needs the wave tile 64 columns wide, C
+// 16-byte aligned with ldc*sizeof(out) a multiple of 16, and the LDS free
+// (every wave past its last LDS read of the main loop).  `lds_bytes` is the
+// LDS the kernel owns; the wave tile is staged in passes of as many rows as
+// fit.
+// Region layout: row-major, 64 elements per row; the 16-byte chunk index is
+// XORed with ((row >> 2) & 1) * (chunks per row / 2), so the two 32-lane
+// halves of an accumulator write (rows r and r + 4, same columns) land in
+// different halves of the bank line.  The 16-lane phases of the reads cover
+// one row each: conflict-free.
+template <class T, int OUT, int LDS_BYTES>
+__device__ __forceinline__ void epilogue_lds(void *C, const v16f32 (&acc)[T::FM][T::FN], char *lds,
+                                             int M, int N, int64_t ldc, int m0, int n0, int wm,
+                                             int wn, int wave, int lane) {
+  static_assert(T::TN == 64, "wave tile 64 columns wide");
+  typedef typename OutElem<OUT>::type E;
+  constexpr int ESZ = sizeof(E);
+  constexpr int ROWB = T::TN * ESZ;                          // 256 (fp32) or 128 bytes
+  constexpr int CPR = ROWB / 16;                             // 16-byte chunks per row
+  constexpr int WAVES = T::WM * T::WN;
+  constexpr int FIT = LDS_BYTES / (WAVES * ROWB);            // rows per wave that fit
+  constexpr int PR = FIT >= T::TM ? T::TM : (FIT >= 64 ? 64 : 32);   // rows per pass
+  static_assert(PR % 32 == 0 && T::TM % PR == 0 && WAVES * PR * ROWB <= LDS_BYTES, "staging fits");
+  constexpr int RPI = 64 * 16 / ROWB;                        // rows per 64-lane read
+  char *mine = lds + wave * PR * ROWB;
+  auto off = [&](int row, int chunk) {
+    return row * ROWB + 16 * (chunk ^ (((row >> 2) & 1) * (CPR / 2)));
+  };
+  const int grow0 = m0 + wm * T::TM;
+  const int gcol0 = n0 + wn * T::TN;
+#pragma unroll
+  for (int pass = 0; pass < T::TM / PR; pass++) {
+    // accumulator blocks i of this pass: rows 32*i .. 32*i + 31 of the wave tile
+#pragma unroll
+    for (int i = pass * PR / 32; i < (pass + 1) * PR / 32; i++)
+#pragma unroll
+      for (int j = 0; j < T::FN; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int row = 32 * i - pass * PR + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = 32 * j + (lane & 31);
+          *(E *)(mine + off(row, col * ESZ / 16) + (col * ESZ) % 16) = (E)acc[i][j][r];
+        }
+    // The reads below return rows written by other lanes of this wave: LDS
+    // executes a wave's instructions in order, so no barrier is needed.
+#pragma unroll
+    for (int it = 0; it < PR / RPI; it++) {
+      const int row = it * RPI + lane / CPR;
+      const int chunk = lane % CPR;
+      const u32x4 v = *(const u32x4 *)(mine + off(row, chunk));
+      const int grow = grow0 + pass * PR + row;
+      const int gcol = gcol0 + chunk * (16 / ESZ);
+      if (grow < M) {
+        E *dst = (E *)C + (int64_t)grow * ldc + gcol;
+        if (gcol + 16 / ESZ <= N) {
+          __builtin_nontemporal_store(v, (u32x4 *)dst);
+        } else {
+          const E *e = (const E *)&v;
+#pragma unroll
+          for (int q = 0; q < 16 / ESZ; q++)
+            if (gcol + q < N) __builtin_nontemporal_store(e[q], dst + q);
+        }
+      }
+    }
   }
 }
 

@@ -162,7 +162,7 @@ template <class T, int LA, int LB, int IN, int OUT>
 __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
-    uint32_t a_bytes, uint32_t b_bytes) {
+    uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   using OA = OperandTile<T::BM, T::BK, LA, T::NT>;
   using OB = OperandTile<T::BN, T::BK, LB, T::NT>;
   using F = Frags<T, OA, OB>;
@@ -248,6 +248,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     mfma_block<T, IN>(acc, nxt);
   }
 
+  if constexpr (T::TN == 64) {
+    if (c_vec) {
+      __syncthreads();                     // every wave is past its last LDS read
+      epilogue_lds<T, OUT, 2 * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+      return;
+    }
+  }
   epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
 }
 

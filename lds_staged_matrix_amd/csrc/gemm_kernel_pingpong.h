@@ -60,7 +60,7 @@ template <class T, int LA, int LB, int IN, int OUT>
 __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
-    uint32_t a_bytes, uint32_t b_bytes) {
+    uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
   constexpr int LOADERS = T::NT / 2;                     // group 0 issues every load
   using OA = OperandTile<T::BM, T::BK, LA, LOADERS>;
@@ -201,7 +201,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     }
   }
 
-  epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
+  // The LDS is free once every wave is past its last fragment read.
+  if (c_vec) {
+    __syncthreads();
+    epilogue_lds<T, OUT, 2 * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+  } else {
+    epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
+  }
 }
 
 }  // namespace lsm

@@ -158,6 +158,29 @@ def test_big_tile_ragged_integer_exact(la, lb):
     H.assert_exact(C[rows, cols], H.oracle_entries(p, rows, cols), lsm.GEMM_BF16_F32, "entries")
 
 
+# The LDS-staged epilogue (16-byte C stores, used when C rows are 16-byte
+# aligned): ragged M and N edges with ldc = N, every output type, on the
+# 256 x 256 ping-pong kernel and the 128 x 128 kernel.
+LDS_EPI = [(4100, 4104, 136), (2050, 2056, 264), (2048, 2052, 72)]
+
+
+@pytest.mark.parametrize("shape", LDS_EPI)
+@pytest.mark.parametrize("gdtype", ALL_DTYPES)
+def test_lds_staged_epilogue_edges_integer_exact(shape, gdtype):
+    M, N, K = shape
+    for la, lb in (ALL_LAYOUTS if gdtype == lsm.GEMM_BF16_BF16 else ALL_LAYOUTS[:1]):
+        announce("lds epilogue", M, N, K, la, lb, gdtype)
+        p = H.problem(M, N, K, H.IN_OF[gdtype], la, lb, "int", (111, 112))
+        C = H.run_gpu(p, gdtype, ldc=N, extra_rows=1)
+        H.assert_canary(C, M, N, gdtype)
+        rng = np.random.default_rng(1)
+        for r0, r1 in ((0, 2), (M - 3, M)):
+            H.assert_exact(C[r0:r1, :N], H.oracle_rows(p, r0, r1), gdtype, f"rows {r0}")
+        cols = np.concatenate([np.arange(N - 40, N), rng.integers(0, N, 2000)])
+        rows = rng.integers(0, M, cols.size)
+        H.assert_exact(C[rows, cols], H.oracle_entries(p, rows, cols), gdtype, "entries")
+
+
 def sample_check(p, C, gdtype, exact, rows_sel, n_entries=4000, seed=0):
     rng = np.random.default_rng(seed)
     for r0, r1 in rows_sel:
