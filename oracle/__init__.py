@@ -8,14 +8,16 @@ C = A*B, C[m][n] = sum_k a(m,k) b(k,n) in fp64, loop order m -> k -> n
 ("An educational GEMM ladder for Helios GPUs", section "Educational GEMM
 Ladder", problem statement C = AB; "Level 0 APIs" table: FP32 accumulation of
 BF16 products, converted on store).  Layout 0 = K-contiguous, 1 =
-MN-contiguous; dtype 0 = bf16, 1 = fp16; leading dimensions count elements.
+MN-contiguous; dtype 0 = bf16, 1 = fp16 (two bytes per element), 2 = OCP
+fp8 E4M3 (one byte per element, decode only); leading dimensions count
+elements.
 """
 import ctypes
 import os
 
 import numpy as np
 
-BF16, F16 = 0, 1
+BF16, F16, E4M3 = 0, 1, 2
 K_CONTIG, MN_CONTIG = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_anyp = ctypes.c_void_p
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
@@ -45,17 +48,19 @@ def _load():
     lib.oracle_encode_bf16.restype = ctypes.c_uint16
     lib.oracle_encode_f16.argtypes = [ctypes.c_double]
     lib.oracle_encode_f16.restype = ctypes.c_uint16
-    lib.oracle_decode_array.argtypes = [_u16p, _f64p, _i64, _int]
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e4m3.restype = ctypes.c_double
+    lib.oracle_decode_array.argtypes = [_anyp, _f64p, _i64, _int]
     lib.oracle_decode_array.restype = None
     lib.oracle_encode_array.argtypes = [_f64p, _u16p, _i64, _int]
     lib.oracle_encode_array.restype = None
-    lib.oracle_gemm_rows.argtypes = [_u16p, _u16p, _f64p, _i64, _i64, _i64, _i64, _i64,
+    lib.oracle_gemm_rows.argtypes = [_anyp, _anyp, _f64p, _i64, _i64, _i64, _i64, _i64,
                                      _i64, _int, _int, _int, _i64, _i64, _int]
     lib.oracle_gemm_rows.restype = _int
-    lib.oracle_gemm.argtypes = [_u16p, _u16p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
+    lib.oracle_gemm.argtypes = [_anyp, _anyp, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _int, _int, _int, _int]
     lib.oracle_gemm.restype = _int
-    lib.oracle_gemm_entries.argtypes = [_u16p, _u16p, _i64, _i64, _i64, _i64, _i64, _int,
+    lib.oracle_gemm_entries.argtypes = [_anyp, _anyp, _i64, _i64, _i64, _i64, _i64, _int,
                                         _int, _int, _i64p, _i64p, _i64, _f64p, _int]
     lib.oracle_gemm_entries.restype = _int
     lib.oracle_max_threads.argtypes = []
@@ -68,11 +73,21 @@ def _u16(x):
     return np.ascontiguousarray(np.asarray(x).reshape(-1).view(np.uint16))
 
 
+def _elements(x, dtype):
+    """Contiguous storage of an element array: uint8 for e4m3, uint16 else."""
+    a = np.asarray(x).reshape(-1)
+    return np.ascontiguousarray(a.view(np.uint8) if dtype == E4M3 else a.view(np.uint16))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
 def decode(bits, dtype):
-    """Exact fp64 values of bf16/fp16 bit patterns."""
-    b = _u16(bits)
+    """Exact fp64 values of bf16/fp16 (uint16) or e4m3 (uint8) bit patterns."""
+    b = _elements(bits, dtype)
     out = np.empty(b.size, dtype=np.float64)
-    _load().oracle_decode_array(b, out, b.size, dtype)
+    _load().oracle_decode_array(_ptr(b), out, b.size, dtype)
     return out.reshape(np.shape(bits))
 
 
@@ -87,7 +102,8 @@ def encode(x, dtype):
 def gemm(A, B, M, N, K, lda, ldb, layoutA, layoutB, dtype, threads=0):
     """Full C (M x N, fp64, row-major) from flat bf16/fp16 storage A and B."""
     C = np.empty((M, N), dtype=np.float64)
-    rc = _load().oracle_gemm(_u16(A), _u16(B), C.reshape(-1) if C.size else np.empty(1),
+    a, b = _elements(A, dtype), _elements(B, dtype)
+    rc = _load().oracle_gemm(_ptr(a), _ptr(b), C.reshape(-1) if C.size else np.empty(1),
                              M, N, K, lda, ldb, max(N, 1), layoutA, layoutB, dtype, threads)
     if rc:
         raise ValueError("oracle_gemm: invalid arguments")
@@ -98,7 +114,8 @@ def gemm_rows(A, B, M, N, K, lda, ldb, layoutA, layoutB, dtype, row_begin, row_e
               threads=0):
     """Rows [row_begin, row_end) of C."""
     C = np.empty((row_end - row_begin, N), dtype=np.float64)
-    rc = _load().oracle_gemm_rows(_u16(A), _u16(B), C.reshape(-1) if C.size else np.empty(1),
+    a, b = _elements(A, dtype), _elements(B, dtype)
+    rc = _load().oracle_gemm_rows(_ptr(a), _ptr(b), C.reshape(-1) if C.size else np.empty(1),
                                   M, N, K, lda, ldb, max(N, 1), layoutA, layoutB, dtype,
                                   row_begin, row_end, threads)
     if rc:
@@ -111,7 +128,8 @@ def gemm_entries(A, B, M, N, K, lda, ldb, layoutA, layoutB, dtype, rows, cols, t
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
     c = np.ascontiguousarray(np.asarray(cols, dtype=np.int64).reshape(-1))
     out = np.empty(r.size, dtype=np.float64)
-    rc = _load().oracle_gemm_entries(_u16(A), _u16(B), M, N, K, lda, ldb, layoutA, layoutB,
+    a, b = _elements(A, dtype), _elements(B, dtype)
+    rc = _load().oracle_gemm_entries(_ptr(a), _ptr(b), M, N, K, lda, ldb, layoutA, layoutB,
                                      dtype, r, c, r.size, out, threads)
     if rc:
         raise ValueError("oracle_gemm_entries: invalid arguments")

@@ -36,13 +36,18 @@
  * is used:
  *     bf16: 1 sign, 8 exponent (bias 127), 7 fraction bits
  *     fp16: 1 sign, 5 exponent (bias 15), 10 fraction bits
+ *     e4m3: 1 sign, 4 exponent (bias 7), 3 fraction bits, one byte per
+ *           element; the OCP 8-bit "E4M3" encoding, which has no infinities:
+ *           exponent 15 with fraction 7 is NaN and every other pattern is
+ *           finite (largest 448).  Only decoded: the oracle never produces
+ *           fp8 outputs.
  */
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 #include <omp.h>
 
-enum { ORACLE_BF16 = 0, ORACLE_F16 = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_F16 = 1, ORACLE_E4M3 = 2 };
 enum { ORACLE_K_CONTIG = 0, ORACLE_MN_CONTIG = 1 };
 
 /* Decode a binary16-family pattern with `fbits` fraction bits and `ebits`
@@ -103,20 +108,41 @@ static uint16_t encode_small_float(double x, int ebits, int fbits)
     return (uint16_t)(sign | ((uint32_t)(e2 + bias) << fbits) | mant);
 }
 
+/* OCP E4M3: as the binary16 family for e < 15; e == 15 is a normal binade too,
+ * except the all-ones pattern, which is NaN. */
+double oracle_decode_e4m3(uint8_t bits)
+{
+    const int sign = (bits >> 7) & 1;
+    const int e = (bits >> 3) & 15;
+    const int f = bits & 7;
+    double v;
+    if (e == 15 && f == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, 1 - 7 - 3);             /* subnormal: f * 2^-9 */
+    else
+        v = ldexp((double)(8 + f), e - 7 - 3);       /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 double oracle_decode_bf16(uint16_t bits) { return decode_small_float(bits, 8, 7); }
 double oracle_decode_f16(uint16_t bits) { return decode_small_float(bits, 5, 10); }
 uint16_t oracle_encode_bf16(double x) { return encode_small_float(x, 8, 7); }
 uint16_t oracle_encode_f16(double x) { return encode_small_float(x, 5, 10); }
 
-static double decode(uint16_t bits, int dtype)
+/* Element i of a bf16/fp16 (two bytes each) or e4m3 (one byte) array. */
+static double element(const void *p, int64_t i, int dtype)
 {
+    if (dtype == ORACLE_E4M3)
+        return oracle_decode_e4m3(((const uint8_t *)p)[i]);
+    const uint16_t bits = ((const uint16_t *)p)[i];
     return dtype == ORACLE_F16 ? oracle_decode_f16(bits) : oracle_decode_bf16(bits);
 }
 
-void oracle_decode_array(const uint16_t *in, double *out, int64_t n, int dtype)
+void oracle_decode_array(const void *in, double *out, int64_t n, int dtype)
 {
     for (int64_t i = 0; i < n; i++)
-        out[i] = decode(in[i], dtype);
+        out[i] = element(in, i, dtype);
 }
 
 void oracle_encode_array(const double *in, uint16_t *out, int64_t n, int dtype)
@@ -133,7 +159,7 @@ static int check_args(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
     if ((layoutA != ORACLE_K_CONTIG && layoutA != ORACLE_MN_CONTIG) ||
         (layoutB != ORACLE_K_CONTIG && layoutB != ORACLE_MN_CONTIG))
         return 1;
-    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16)
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16 && dtype != ORACLE_E4M3)
         return 1;
     if (lda < (layoutA == ORACLE_K_CONTIG ? K : M))
         return 1;
@@ -154,7 +180,7 @@ static inline int64_t b_index(int64_t k, int64_t n, int64_t ldb, int layoutB)
 
 /* Rows [row_begin, row_end) of C = A*B, written to C (row row_begin at C[0]).
  * nthreads <= 0 uses every available thread.  Returns 0 on success. */
-int oracle_gemm_rows(const uint16_t *A, const uint16_t *B, double *C,
+int oracle_gemm_rows(const void *A, const void *B, double *C,
                      int64_t M, int64_t N, int64_t K,
                      int64_t lda, int64_t ldb, int64_t ldc,
                      int layoutA, int layoutB, int dtype,
@@ -171,15 +197,15 @@ int oracle_gemm_rows(const uint16_t *A, const uint16_t *B, double *C,
         for (int64_t n = 0; n < N; n++)
             crow[n] = 0.0;
         for (int64_t k = 0; k < K; k++) {
-            const double a = decode(A[a_index(m, k, lda, layoutA)], dtype);
+            const double a = element(A, a_index(m, k, lda, layoutA), dtype);
             for (int64_t n = 0; n < N; n++)
-                crow[n] += a * decode(B[b_index(k, n, ldb, layoutB)], dtype);
+                crow[n] += a * element(B, b_index(k, n, ldb, layoutB), dtype);
         }
     }
     return 0;
 }
 
-int oracle_gemm(const uint16_t *A, const uint16_t *B, double *C,
+int oracle_gemm(const void *A, const void *B, double *C,
                 int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                 int layoutA, int layoutB, int dtype, int nthreads)
 {
@@ -189,7 +215,7 @@ int oracle_gemm(const uint16_t *A, const uint16_t *B, double *C,
 
 /* Individual entries C[rows[i]][cols[i]], each the k-ordered fp64 dot product;
  * used to check outputs of problems too large for the full loop. */
-int oracle_gemm_entries(const uint16_t *A, const uint16_t *B,
+int oracle_gemm_entries(const void *A, const void *B,
                         int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                         int layoutA, int layoutB, int dtype,
                         const int64_t *rows, const int64_t *cols, int64_t count,
@@ -207,8 +233,8 @@ int oracle_gemm_entries(const uint16_t *A, const uint16_t *B,
         const int64_t m = rows[i], n = cols[i];
         double s = 0.0;
         for (int64_t k = 0; k < K; k++)
-            s += decode(A[a_index(m, k, lda, layoutA)], dtype) *
-                 decode(B[b_index(k, n, ldb, layoutB)], dtype);
+            s += element(A, a_index(m, k, lda, layoutA), dtype) *
+                 element(B, b_index(k, n, ldb, layoutB), dtype);
         out[i] = s;
     }
     return 0;

@@ -14,8 +14,10 @@ Distributions:
   normal  : Box-Muller on two consecutive draws, u1 = ((x1 >> 11) + 1) * 2^-53
             in (0, 1], u2 = (x2 >> 11) * 2^-53, value sqrt(-2 ln u1) cos(2 pi u2)
   int     : ((x >> 32) mod 5) - 2, entries in {-2, ..., 2}
-Values are rounded to fp32, then to bf16/fp16 with round-to-nearest-even by
-torch/numpy's own conversions.
+Values are rounded to fp32, then to bf16/fp16/fp8 E4M3 (OCP, the encoding
+without infinities) with round-to-nearest-even by torch/numpy's own
+conversions.  bf16 and fp16 elements are stored as uint16 bit patterns, e4m3
+elements as uint8.
 
 The logical matrices are A[m][k] (M x K) and B[k][n] (K x N), drawn in
 row-major order, then stored in the requested contiguity:
@@ -29,9 +31,10 @@ from dataclasses import dataclass, field
 import numpy as np
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
-BF16, F16 = "bf16", "f16"
+BF16, F16, E4M3 = "bf16", "f16", "e4m3"
 K_CONTIG, MN_CONTIG = "K", "MN"
-NAN_BITS = {BF16: 0x7FC0, F16: 0x7E00}
+NAN_BITS = {BF16: 0x7FC0, F16: 0x7E00, E4M3: 0x7F}
+STORAGE = {BF16: np.uint16, F16: np.uint16, E4M3: np.uint8}
 
 
 def splitmix64(seed: int, n: int) -> np.ndarray:
@@ -66,7 +69,8 @@ def draw(seed: int, n: int, dist: str, scale: float = 1.0) -> np.ndarray:
 
 
 def quantize(values: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 -> fp32 -> bf16/fp16 bits (uint16), round to nearest even."""
+    """float64 -> fp32 -> bf16/fp16 bits (uint16) or e4m3 bits (uint8), round
+    to nearest even."""
     f32 = np.ascontiguousarray(np.asarray(values, dtype=np.float32))
     if dtype == F16:
         return f32.astype(np.float16).view(np.uint16)
@@ -74,20 +78,27 @@ def quantize(values: np.ndarray, dtype: str) -> np.ndarray:
         import torch
         t = torch.from_numpy(f32).to(torch.bfloat16)
         return t.view(torch.int16).numpy().view(np.uint16)
+    if dtype == E4M3:
+        import torch
+        if np.any(np.abs(f32) > 448.0):
+            raise ValueError("value beyond the e4m3 range")
+        t = torch.from_numpy(f32).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy()
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def store(logical: np.ndarray, transpose: bool, ld: int, dtype: str) -> np.ndarray:
     """Lay out a logical (R x C) bit matrix row-major with leading dimension
-    `ld`, transposed first if `transpose`.  Returns flat uint16 storage holding
-    rows*ld - (ld - extent) elements, padding filled with NaN bits."""
+    `ld`, transposed first if `transpose`.  Returns flat uint16 (uint8 for
+    e4m3) storage holding rows*ld - (ld - extent) elements, padding filled with
+    NaN bits."""
     mat = logical.T if transpose else logical
     rows, extent = mat.shape
     if ld < extent:
         raise ValueError("leading dimension below the contiguous extent")
     if rows == 0:
-        return np.zeros(0, dtype=np.uint16)
-    buf = np.full((rows, ld), NAN_BITS[dtype], dtype=np.uint16)
+        return np.zeros(0, dtype=STORAGE[dtype])
+    buf = np.full((rows, ld), NAN_BITS[dtype], dtype=STORAGE[dtype])
     buf[:, :extent] = mat
     flat = buf.reshape(-1)
     return np.ascontiguousarray(flat[: (rows - 1) * ld + extent])
@@ -104,7 +115,7 @@ class Problem:
     layoutB: str
     lda: int
     ldb: int
-    A: np.ndarray = field(repr=False)   # flat uint16 storage
+    A: np.ndarray = field(repr=False)   # flat uint16 (uint8 for e4m3) storage
     B: np.ndarray = field(repr=False)
     A_logical: np.ndarray = field(repr=False, default=None)   # M x K bits
     B_logical: np.ndarray = field(repr=False, default=None)   # K x N bits
@@ -158,4 +169,8 @@ WORKLOADS = {
     "bf16_skinny_32x16384x8192_nn_bf16": dict(M=32, N=16384, K=8192, dtype=BF16, out="bf16",
                                               layouts=[("K", "MN")], dist="uniform", scale=1.0,
                                               seeds=(5001, 5002)),
+    # The fp8 variant (the same LDS machinery with 1-byte elements): the
+    # headline shape and layout with OCP E4M3 inputs.
+    "e4m3_8192_nn_f32": dict(M=8192, N=8192, K=8192, dtype=E4M3, out="f32", layouts=[("K", "MN")],
+                             dist="normal", scale=1.0, seeds=(6001, 6002)),
 }

@@ -20,7 +20,7 @@ import synth
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 LAYOUTS = [(la, lb) for la in ("K", "MN") for lb in ("K", "MN")]
 OL = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
-OD = {synth.BF16: oracle.BF16, synth.F16: oracle.F16}
+OD = {synth.BF16: oracle.BF16, synth.F16: oracle.F16, synth.E4M3: oracle.E4M3}
 
 
 def run_oracle(p: synth.Problem, threads=0):
@@ -140,6 +140,62 @@ def test_encode_decode_round_trip(oracle_lib):
         vals = oracle.decode(bits, d)
         keep = ~np.isnan(vals)
         assert np.array_equal(oracle.encode(vals[keep], d), bits[keep])
+
+
+def test_decode_e4m3_all_patterns_vs_torch(oracle_lib):
+    bits = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    got = oracle.decode(bits, oracle.E4M3)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2                                  # 0x7F and 0xFF only
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("bits,value", [
+    # OCP 8-bit E4M3 (bias 7, no infinities): 1.0, the largest finite value,
+    # the smallest normal and subnormal, -0 and the values next to 1.
+    (0x38, 1.0), (0x7E, 448.0), (0xFE, -448.0), (0x08, 2.0 ** -6), (0x01, 2.0 ** -9),
+    (0x07, 7 * 2.0 ** -9), (0x80, -0.0), (0x39, 1.125), (0x30, 0.5), (0x40, 2.0),
+    (0x78, 256.0), (0x77, 240.0)])
+def test_decode_e4m3_format_definition(oracle_lib, bits, value):
+    got = oracle.decode(np.array([bits], dtype=np.uint8), oracle.E4M3)[0]
+    assert got == value and np.signbit(got) == np.signbit(value)
+
+
+def test_e4m3_gemm_matches_exact_rationals(oracle_lib):
+    # every finite e4m3 value is a dyadic rational; random codes (including
+    # subnormals and the largest values) in all layouts
+    rng = np.random.default_rng(8)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for trial, (la, lb) in enumerate(LAYOUTS * 3):
+        M, N, K = (int(x) for x in rng.integers(1, 7, size=3))
+        a = rng.choice(finite, size=(M, K))
+        b = rng.choice(finite, size=(K, N))
+        p = synth.layout_problem(a, b, synth.E4M3, la, lb, pad_a=trial % 3, pad_b=(trial + 1) % 3)
+        av = oracle.decode(a, oracle.E4M3).tolist()
+        bv = oracle.decode(b, oracle.E4M3).tolist()
+        exact = exact_product(av, bv)
+        C = run_oracle(p)
+        for m in range(M):
+            for n in range(N):
+                bound = K * 2.0 ** -53 * sum(abs(av[m][k] * bv[k][n]) for k in range(K))
+                assert abs(Fraction(C[m, n]) - exact[m][n]) <= Fraction(bound)
+
+
+def test_e4m3_integer_gemm_is_exact_and_layout_free(oracle_lib):
+    M, N, K = 13, 10, 17
+    outs = []
+    for la, lb in LAYOUTS:
+        p = synth.make_problem(M, N, K, synth.E4M3, la, lb, "int", 17, 18, pad_a=2, pad_b=3)
+        ai = oracle.decode(p.A_logical, oracle.E4M3).astype(int)
+        bi = oracle.decode(p.B_logical, oracle.E4M3).astype(int)
+        want = [[int(sum(int(ai[m, k]) * int(bi[k, n]) for k in range(K))) for n in range(N)]
+                for m in range(M)]
+        outs.append(run_oracle(p))
+        assert outs[-1].tolist() == want
+    assert all(np.array_equal(o, outs[0]) for o in outs)
 
 
 # ---------------------------------------------------------------- GEMM pins
