@@ -29,10 +29,13 @@ import synth  # noqa: E402
 METRIC = "bf16 GEMM TFLOP/s + % of MFMA peak; LDS bank-conflict rate (1 MI355X)"
 # MI355X dense MFMA peak for bf16/fp16 inputs: 256 CUs x 2.4 GHz x 4096 flop/clk/CU
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 2516.6
+# MI355X dense MFMA peak for fp8 inputs: twice the bf16 rate
+PEAK_FP8_TFLOPS = 256 * 2.4e9 * 8192 / 1e12           # 5033.2
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "bf16_8192_nn_f32"
 KERNEL_DIR = "lds_staged_matrix_amd/csrc"
-DTYPE_CODE = {("bf16", "f32"): 0, ("bf16", "bf16"): 1, ("f16", "f16"): 2, ("f16", "f32"): 3}
+DTYPE_CODE = {("bf16", "f32"): 0, ("bf16", "bf16"): 1, ("f16", "f16"): 2, ("f16", "f32"): 3,
+              ("e4m3", "f32"): 4, ("e4m3", "bf16"): 5}
 
 
 def log(*a):
@@ -84,8 +87,9 @@ def make_inputs(w, layout):
     la, lb = layout
     p = synth.make_problem(w["M"], w["N"], w["K"], w["dtype"], la, lb, w["dist"], w["seeds"][0],
                            w["seeds"][1], w["scale"])
-    A = torch.from_numpy(p.A.view(np.int16)).cuda()
-    B = torch.from_numpy(p.B.view(np.int16)).cuda()
+    raw = (lambda x: x.view(np.int8)) if w["dtype"] == synth.E4M3 else (lambda x: x.view(np.int16))
+    A = torch.from_numpy(raw(p.A)).cuda()
+    B = torch.from_numpy(raw(p.B)).cuda()
     return p, A, B
 
 
@@ -93,7 +97,7 @@ def cpu_baseline(p, rows):
     """The oracle, as it is, on `rows` full rows of C of the same problem."""
     import oracle
     ol = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
-    od = {synth.BF16: oracle.BF16, synth.F16: oracle.F16}
+    od = {synth.BF16: oracle.BF16, synth.F16: oracle.F16, synth.E4M3: oracle.E4M3}
     threads = oracle.max_threads()
     t0 = time.perf_counter()
     oracle.gemm_rows(p.A, p.B, p.M, p.N, p.K, p.lda, p.ldb, ol[p.layoutA], ol[p.layoutB],
@@ -194,7 +198,10 @@ def main():
     flops = 2.0 * M * N * K
     out_bytes = 4 if w["out"] == "f32" else 2
     alg_bytes = 2.0 * (M * K + K * N) + out_bytes * M * N
-    hbm_bound = flops / alg_bytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    in_bytes = 1 if w["dtype"] == synth.E4M3 else 2
+    alg_bytes = in_bytes * (M * K + K * N) + out_bytes * M * N
+    peak_tflops = PEAK_FP8_TFLOPS if w["dtype"] == synth.E4M3 else PEAK_BF16_TFLOPS
+    hbm_bound = flops / alg_bytes < (peak_tflops * 1e12) / (PEAK_HBM_GBS * 1e9)
 
     # Same kernel with cold caches (the pages' method): before each launch,
     # outside its events, read 1 GiB so that L2 and the 256 MB Infinity Cache
@@ -221,8 +228,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
         achieved = flops / (kavg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(PEAK_BF16_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak_tflops, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4)}
     src_hash = kernel_source_hash()
     roof["traffic"] = read_traffic(args.workload, src_hash) if layout == tuple(w["layouts"][0]) \
         else None
@@ -231,7 +238,8 @@ def main():
         f"flushed-cache median {np.median(fl_ms) if fl_ms else float('nan'):.4f} ms; "
         f"wall per step {ms_per_step:.4f} ms")
     log(f"kernel TFLOP/s {flops / (kavg * 1e-3) / 1e12:.1f}, "
-        f"{flops / (kavg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS * 100:.1f}% of dense bf16 peak; "
+        f"{flops / (kavg * 1e-3) / 1e12 / peak_tflops * 100:.1f}% of the dense "
+        f"{'fp8' if in_bytes == 1 else 'bf16'} peak; "
         f"algorithmic GB/s {alg_bytes / (kavg * 1e-3) / 1e9:.1f}")
 
     cpu = None
@@ -246,7 +254,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w["dtype"] == synth.BF16 else "f16", "data": "synthetic",
+        "dtype": w["dtype"], "data": "synthetic",
         "config": {"workload": f"{w['dtype']} GEMM M={M} N={N} K={K}, A "
                                f"{'K' if layout[0] == 'K' else 'M'}-contiguous, B "
                                f"{'K' if layout[1] == 'K' else 'N'}-contiguous, {w['out']} output, "

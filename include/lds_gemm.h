@@ -54,12 +54,19 @@ enum gemm_layout {
     GEMM_MN_CONTIG = 1   /* M (for A) or N (for B) is contiguous           */
 };
 
-/* Element types, named input_output; accumulation is always fp32. */
+/* Element types, named input_output; accumulation is always fp32.
+ * E4M3 is the OCP 8-bit floating-point format with 4 exponent bits (bias 7),
+ * 3 fraction bits and no infinities, one byte per element; its products run
+ * on the gfx950 fp8 matrix instruction ("Lds Optimization", "MFMA Transpose
+ * Load from LDS (gfx950 only)": DS_READ_B64_TR_B8 feeds 8-bit MFMA
+ * operands). */
 enum gemm_dtype {
     GEMM_BF16_F32 = 0,   /* bf16 A, B;  fp32 C                             */
     GEMM_BF16_BF16 = 1,  /* bf16 A, B;  bf16 C (round to nearest even)     */
     GEMM_F16_F16 = 2,    /* fp16 A, B;  fp16 C (round to nearest even)     */
-    GEMM_F16_F32 = 3     /* fp16 A, B;  fp32 C                             */
+    GEMM_F16_F32 = 3,    /* fp16 A, B;  fp32 C                             */
+    GEMM_E4M3_F32 = 4,   /* fp8 E4M3 A, B;  fp32 C                         */
+    GEMM_E4M3_BF16 = 5   /* fp8 E4M3 A, B;  bf16 C (round to nearest even) */
 };
 
 enum gemm_status {
@@ -76,8 +83,11 @@ enum gemm_status {
 int gemm_create(gemm_handle_t *out);
 
 /* Enqueue C <- A*B on `stream` (0 = the device's null stream).
- *   A, B       device pointers to bf16/fp16 elements, 16-byte aligned;
- *              lda/ldb must be multiples of 8 elements (16 bytes).
+ *   A, B       device pointers to bf16/fp16 (2-byte) or E4M3 (1-byte)
+ *              elements, 16-byte aligned; lda/ldb must be multiples of 16
+ *              bytes (8 bf16/fp16 or 16 E4M3 elements).  E4M3 inputs further
+ *              need the contiguous extents (K or M of A, N or K of B) to be
+ *              multiples of 16 elements, else GEMM_ERR_UNSUPPORTED.
  *   C          device pointer to fp32 (4-byte aligned) or bf16/fp16
  *              (2-byte aligned) elements; must not overlap A or B.
  *   M, N, K    sizes, 0 <= size < 2^30; lda, ldb, ldc < 2^40.  M == 0 or N == 0 is a no-op;

@@ -14,7 +14,8 @@ import os
 
 __all__ = [
     "GEMM_K_CONTIG", "GEMM_MN_CONTIG",
-    "GEMM_BF16_F32", "GEMM_BF16_BF16", "GEMM_F16_F16", "GEMM_F16_F32",
+    "GEMM_BF16_F32", "GEMM_BF16_BF16", "GEMM_F16_F16", "GEMM_F16_F32", "GEMM_E4M3_F32",
+    "GEMM_E4M3_BF16",
     "GEMM_OK", "GEMM_ERR_INVALID_ARG", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_DEVICE",
     "GEMM_ERR_LAUNCH", "GemmError", "library_path", "load_library", "gemm_create",
     "gemm_run", "gemm_destroy", "gemm_status_str", "EXPORTED_SYMBOLS", "Library",
@@ -23,6 +24,7 @@ __all__ = [
 
 GEMM_K_CONTIG, GEMM_MN_CONTIG = 0, 1
 GEMM_BF16_F32, GEMM_BF16_BF16, GEMM_F16_F16, GEMM_F16_F32 = 0, 1, 2, 3
+GEMM_E4M3_F32, GEMM_E4M3_BF16 = 4, 5
 GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_DEVICE, GEMM_ERR_LAUNCH = range(5)
 EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_status_str")
 

@@ -45,6 +45,11 @@ using PingPong = Tile<256, 256, 64, 2, 4, 8>;
 #define LSM_RING_STAGES 6
 #endif
 using SkinnyStream = SkinnyTile<32, 64, 128, LSM_RING_STAGES>;
+// 8-bit (E4M3) inputs: the same tiles in bytes, so BK doubles in elements.
+using PingPong8 = Tile<256, 256, 128, 2, 4, 8>;
+using DmaMid8 = Tile<128, 128, 128, 2, 2, 8>;
+using DmaSmall8 = Tile<64, 64, 128, 2, 2, 8>;
+using SkinnyStream8 = SkinnyTile<32, 64, 256, LSM_RING_STAGES>;
 
 struct Args {
   const uint16_t *A;
@@ -133,18 +138,26 @@ static hipError_t launch_dtype(const Args &a, int la, int lb, int dtype, hipStre
   }
 }
 
+template <class T, int DMA>
+static hipError_t launch_fp8(const Args &a, int la, int lb, int dtype, hipStream_t s) {
+  if (dtype == GEMM_E4M3_F32) return launch_layout<T, DMA, IN_E4M3, OUT_F32>(a, la, lb, s);
+  return launch_layout<T, DMA, IN_E4M3, OUT_BF16>(a, la, lb, s);
+}
+
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The direct-to-LDS kernel needs whole 16-byte chunks along each operand's
+static bool is_fp8(int dtype) { return dtype == GEMM_E4M3_F32 || dtype == GEMM_E4M3_BF16; }
+
+// The direct-to-LDS kernels need whole 16-byte chunks along each operand's
 // contiguous dimension, and byte offsets (footprint plus one tile of rows of
-// overhang, plus a K advance) below 2^31 for its 32-bit buffer offsets.
-static bool dma_ok(const Args &a, int la, int lb) {
+// overhang, plus a K advance) below 2^31 for their 32-bit buffer offsets.
+static bool dma_ok(const Args &a, int la, int lb, int64_t es) {
   const int64_t a_inner = la == KC ? a.K : a.M, a_outer = la == KC ? a.M : a.K;
   const int64_t b_inner = lb == MNC ? a.N : a.K, b_outer = lb == MNC ? a.K : a.N;
   const int64_t lim = (int64_t)1 << 31;
-  return a_inner % 8 == 0 && b_inner % 8 == 0 &&
-         (a_outer + 512) * a.lda * 2 + 2 * (int64_t)a.K < lim &&
-         (b_outer + 512) * a.ldb * 2 + 2 * (int64_t)a.K < lim;
+  return (a_inner * es) % 16 == 0 && (b_inner * es) % 16 == 0 &&
+         (a_outer + 512) * a.lda * es + es * (int64_t)a.K < lim &&
+         (b_outer + 512) * a.ldb * es + es * (int64_t)a.K < lim;
 }
 
 // Shape classes.  M <= 32 takes the split-K ring kernel (HBM-bound).
@@ -153,10 +166,18 @@ static bool dma_ok(const Args &a, int la, int lb) {
 // latency-bound K loop per workgroup; more workgroups hide more of it).
 // Shapes whose contiguous extents are not whole 16-byte chunks (dma_ok()
 // false) take the register-staged kernel of the same class.
+// 8-bit inputs run on the direct-to-LDS kernels only (gemm_run rejects fp8
+// shapes those cannot take).
 static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t s) {
-  const bool dma = dma_ok(a, la, lb);
   const int64_t t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   const int64_t t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
+  if (is_fp8(dtype)) {
+    if (a.M <= 32) return launch_fp8<SkinnyStream8, SKINNY>(a, la, lb, dtype, s);
+    if (t256 >= 256) return launch_fp8<PingPong8, PINGPONG>(a, la, lb, dtype, s);
+    if (t128 >= 256) return launch_fp8<DmaMid8, DMA>(a, la, lb, dtype, s);
+    return launch_fp8<DmaSmall8, DMA>(a, la, lb, dtype, s);
+  }
+  const bool dma = dma_ok(a, la, lb, 2);
   if (dma) {
     if (a.M <= 32) return launch_dtype<SkinnyStream, SKINNY>(a, la, lb, dtype, s);
     if (t256 >= 256) return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
@@ -217,7 +238,7 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, 
   if ((layoutA != GEMM_K_CONTIG && layoutA != GEMM_MN_CONTIG) ||
       (layoutB != GEMM_K_CONTIG && layoutB != GEMM_MN_CONTIG))
     return GEMM_ERR_INVALID_ARG;
-  if (dtype < GEMM_BF16_F32 || dtype > GEMM_F16_F32) return GEMM_ERR_INVALID_ARG;
+  if (dtype < GEMM_BF16_F32 || dtype > GEMM_E4M3_BF16) return GEMM_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return GEMM_OK;
   if (!C || (K > 0 && (!A || !B))) return GEMM_ERR_INVALID_ARG;
 
@@ -234,29 +255,34 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, 
   if (ceil_div(M, 32) * ceil_div(N, 64) >= ((int64_t)1 << 31)) return GEMM_ERR_UNSUPPORTED;
   if (lda >= ((int64_t)1 << 40) || ldb >= ((int64_t)1 << 40) || ldc >= ((int64_t)1 << 40))
     return GEMM_ERR_UNSUPPORTED;
-  const int64_t out_size = (dtype == GEMM_BF16_F32 || dtype == GEMM_F16_F32) ? 4 : 2;
+  const int64_t out_size =
+      (dtype == GEMM_BF16_F32 || dtype == GEMM_F16_F32 || dtype == GEMM_E4M3_F32) ? 4 : 2;
+  const int64_t es = is_fp8(dtype) ? 1 : 2;             // input element bytes
   if (K > 0) {
-    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || (lda & 7) || (ldb & 7))
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15) || ((lda * es) & 15) || ((ldb * es) & 15))
       return GEMM_ERR_UNSUPPORTED;
   }
   if ((uintptr_t)C & (uintptr_t)(out_size - 1)) return GEMM_ERR_UNSUPPORTED;
 
   const int64_t c_bytes = ((M - 1) * ldc + N) * out_size;
   if (K > 0) {
-    const int64_t a_bytes = ((a_outer - 1) * lda + a_inner) * 2;
-    const int64_t b_bytes = ((b_outer - 1) * ldb + b_inner) * 2;
+    const int64_t a_bytes = ((a_outer - 1) * lda + a_inner) * es;
+    const int64_t b_bytes = ((b_outer - 1) * ldb + b_inner) * es;
     if (ranges_overlap(C, c_bytes, A, a_bytes) || ranges_overlap(C, c_bytes, B, b_bytes))
       return GEMM_ERR_INVALID_ARG;
   }
 
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return GEMM_ERR_DEVICE;
-
-  const int64_t a_fp = K > 0 ? ((a_outer - 1) * lda + a_inner) * 2 : 0;
-  const int64_t b_fp = K > 0 ? ((b_outer - 1) * ldb + b_inner) * 2 : 0;
+  const int64_t a_fp = K > 0 ? ((a_outer - 1) * lda + a_inner) * es : 0;
+  const int64_t b_fp = K > 0 ? ((b_outer - 1) * ldb + b_inner) * es : 0;
   const Args args{(const uint16_t *)A, (const uint16_t *)B, C, (int)M, (int)N, (int)K,
                   lda, ldb, ldc, (uint32_t)(a_fp < ((int64_t)1 << 31) ? a_fp : 0),
                   (uint32_t)(b_fp < ((int64_t)1 << 31) ? b_fp : 0)};
+  // 8-bit inputs need the direct-to-LDS kernels: whole 16-element chunks
+  // along both contiguous extents and 32-bit buffer offsets.
+  if (is_fp8(dtype) && !dma_ok(args, layoutA, layoutB, 1)) return GEMM_ERR_UNSUPPORTED;
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return GEMM_ERR_DEVICE;
   if (dispatch(args, layoutA, layoutB, dtype, stream) != hipSuccess) return GEMM_ERR_LAUNCH;
   return GEMM_OK;
 }

@@ -23,12 +23,30 @@ typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef _Float16 v8f16 __attribute__((ext_vector_type(8)));
 typedef float v16f32 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v8i32 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 typedef __attribute__((address_space(3))) void lds_void;
 
 enum { KC = 0, MNC = 1 };                       // operand contiguity, values of enum gemm_layout
-enum { IN_BF16 = 0, IN_F16 = 1 };
+enum { IN_BF16 = 0, IN_F16 = 1, IN_E4M3 = 2 };
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
+
+// Input element types: bytes per element, k per MFMA and the per-lane
+// operand fragment.  16-bit inputs use v_mfma_f32_32x32x16_{bf16,f16} (8
+// elements, 16 bytes per lane); OCP fp8 E4M3 inputs use
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (32 elements, 32 bytes).
+template <int IN>
+struct InT {
+  static constexpr int ES = 2, KSTEP = 16;
+  typedef v8i16 frag;
+};
+template <>
+struct InT<IN_E4M3> {
+  static constexpr int ES = 1, KSTEP = 64;
+  typedef v8i32 frag;
+};
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int GROUP_M_>
 struct Tile {
@@ -38,7 +56,7 @@ struct Tile {
   static constexpr int NT = WM * WN * 64;                  // threads per workgroup
   static constexpr int TM = BM / WM, TN = BN / WN;         // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;         // 32x32 fragments per wave
-  static constexpr int KSTEPS = BK / 16;                   // MFMA k steps per K tile
+  static constexpr int KSTEPS = BK / 16;                   // MFMA k steps per K tile, 16-bit inputs
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(BK % 16 == 0, "BK must be a multiple of 16");
 };
@@ -46,20 +64,23 @@ struct Tile {
 // Geometry of one operand's LDS tile.  MN is the tile's M (for A) or N (for
 // B) extent.  K-contiguous: MN rows of BK elements.  MN-contiguous: BK rows of
 // MN elements.  "outer" is the strided dimension of the operand in memory,
-// "inner" its unit-stride dimension.  The tile is filled in rounds of NT
-// 16-byte chunks: chunk id = thread + round * NT, numbered row-major.
-template <int MN, int BK, int LAYOUT, int NT>
+// "inner" its unit-stride dimension; ES is the element size in bytes.  The
+// tile is filled in rounds of NT 16-byte chunks: chunk id = thread + round *
+// NT, numbered row-major.
+template <int MN, int BK, int LAYOUT, int NT, int ES_ = 2>
 struct OperandTile {
   static constexpr bool kcontig = LAYOUT == KC;
+  static constexpr int ES = ES_;
   static constexpr int ROWS = kcontig ? MN : BK;                 // outer extent
   static constexpr int INNER = kcontig ? BK : MN;                // inner extent (elements)
-  static constexpr int ROW_BYTES = 2 * INNER;
+  static constexpr int ROW_BYTES = ES * INNER;
+  static constexpr int EPC = 16 / ES;                            // elements per 16-byte chunk
   static constexpr int CPR = ROW_BYTES / 16;                     // 16-byte chunks per row
   static constexpr int BYTES = ROWS * ROW_BYTES;
   static constexpr int CHUNKS = BYTES / 16;
   static constexpr int LOADS = CHUNKS / NT;                      // 16-byte loads per thread
   static constexpr int ROW_STEP = NT / CPR;                      // rows between a thread's loads
-  static constexpr int SWZ_PERIOD = kcontig ? 16 : 4;            // rows after which the swizzle repeats
+  static constexpr int SWZ_PERIOD = kcontig ? 16 : (ES == 2 ? 4 : 8);   // rows per swizzle period
   static_assert(CHUNKS % NT == 0, "tile must split evenly into 16-byte loads");
   static_assert(NT % CPR == 0 && ROW_STEP % SWZ_PERIOD == 0,
                 "a thread's chunks must share one swizzle phase");
@@ -75,8 +96,38 @@ __device__ __forceinline__ v16f32 mfma_32x32x16(v8i16 a, v8i16 b, v16f32 c) {
                                                   __builtin_bit_cast(v8f16, b), c, 0, 0, 0);
 }
 
+// One 32 x 32 MFMA step of the input type: k = 16 (bf16/fp16) or k = 64
+// (E4M3: format code 0 for both operands, E8M0 scales 127 = 2^0).
+template <int IN>
+__device__ __forceinline__ v16f32 mfma_step(typename InT<IN>::frag a, typename InT<IN>::frag b,
+                                            v16f32 c) {
+  if constexpr (IN == IN_E4M3)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  else
+    return mfma_32x32x16<IN>(a, b, c);
+}
+
 // One 32x32x16 operand fragment: lane l gets row/column (l & 31) of the
 // fragment starting at `base`, k = 16*kk + 8*(l >> 5) + 0..7.
+// One 32 x 64 operand fragment of 8-bit elements (k-step kk of the tile).
+template <class OT>
+__device__ __forceinline__ v8i32 read_frag8(const char *lds, int lane, int base, int kk) {
+  if constexpr (OT::kcontig) {
+    const u32x4 lo = *(const u32x4 *)(lds + frag_kc8_offset(lane, base, kk, 0, OT::ROW_BYTES));
+    const u32x4 hi = *(const u32x4 *)(lds + frag_kc8_offset(lane, base, kk, 1, OT::ROW_BYTES));
+    return __builtin_bit_cast(v8i32, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    v2i32 p[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      p[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i32 *)(lds + frag_tr8_offset(lane, base, kk, q, OT::ROW_BYTES)));
+    const auto lo = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
 template <class OT>
 __device__ __forceinline__ v8i16 read_frag(const char *lds, int lane, int base, int kk) {
   if constexpr (OT::kcontig) {
@@ -226,6 +277,22 @@ __device__ __forceinline__ void epilogue_lds(void *C, const v16f32 (&acc)[T::FM]
       }
     }
   }
+}
+
+// Operand fragment for input type IN (k-step kk of the tile).
+template <class OT, int IN>
+__device__ __forceinline__ typename InT<IN>::frag read_frag_in(const char *lds, int lane, int base,
+                                                               int kk) {
+  if constexpr (IN == IN_E4M3)
+    return read_frag8<OT>(lds, lane, base, kk);
+  else
+    return read_frag<OT>(lds, lane, base, kk);
+}
+
+// LDS read instructions per fragment.
+template <class OT, int IN>
+constexpr int frag_reads() {
+  return IN == IN_E4M3 ? (OT::kcontig ? 2 : 4) : (OT::kcontig ? 1 : 2);
 }
 
 }  // namespace lsm

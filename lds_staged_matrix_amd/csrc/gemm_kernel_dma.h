@@ -109,42 +109,42 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int tid, int mn0, int mn_ext
   const int row = loader_row(tid, OT::ROW_BYTES);
   const int pchunk = loader_chunk(tid, OT::ROW_BYTES);
   const int lchunk = pchunk ^ (OT::kcontig ? kc_swizzle(row, OT::ROW_BYTES)
-                                           : mn_swizzle(row, OT::ROW_BYTES));
-  const int inner = 8 * lchunk;
+                                           : mn_swizzle(row, OT::ROW_BYTES, OT::ES));
+  const int inner = OT::EPC * lchunk;                 // first element of the chunk
   inner_out = inner;
   int64_t off;
   if constexpr (OT::kcontig) {
-    off = ((int64_t)(mn0 + row) * ld + inner) * 2;
+    off = ((int64_t)(mn0 + row) * ld + inner) * OT::ES;
   } else {
     if (mn0 + inner >= mn_ext) return kOutOfRange;
-    off = ((int64_t)row * ld + mn0 + inner) * 2;
+    off = ((int64_t)row * ld + mn0 + inner) * OT::ES;
   }
   return off < (int64_t)bytes ? (uint32_t)off : kOutOfRange;
 }
 
-template <class T, class OA, class OB>
+template <class T, int IN>
 struct Frags {
-  v8i16 a[T::FM], b[T::FN];
+  typename InT<IN>::frag a[T::FM], b[T::FN];
 };
 
 // Reads in the order the MFMAs (row-fragment major) consume them: a[0] with
 // every b[j] first, then the remaining a[i].
-template <class T, class OA, class OB>
-__device__ __forceinline__ void read_frags(Frags<T, OA, OB> &f, const char *sA, const char *sB,
+template <class T, int IN, class OA, class OB>
+__device__ __forceinline__ void read_frags(Frags<T, IN> &f, const char *sA, const char *sB,
                                            int lane, int wm, int wn, int kk) {
-  f.a[0] = read_frag<OA>(sA, lane, wm * T::TM, kk);
+  f.a[0] = read_frag_in<OA, IN>(sA, lane, wm * T::TM, kk);
 #pragma unroll
-  for (int j = 0; j < T::FN; j++) f.b[j] = read_frag<OB>(sB, lane, wn * T::TN + 32 * j, kk);
+  for (int j = 0; j < T::FN; j++) f.b[j] = read_frag_in<OB, IN>(sB, lane, wn * T::TN + 32 * j, kk);
 #pragma unroll
-  for (int i = 1; i < T::FM; i++) f.a[i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+  for (int i = 1; i < T::FM; i++) f.a[i] = read_frag_in<OA, IN>(sA, lane, wm * T::TM + 32 * i, kk);
 }
 
-template <class T, int IN, class OA, class OB>
-__device__ __forceinline__ void mfma_block(v16f32 (&acc)[T::FM][T::FN], const Frags<T, OA, OB> &f) {
+template <class T, int IN>
+__device__ __forceinline__ void mfma_block(v16f32 (&acc)[T::FM][T::FN], const Frags<T, IN> &f) {
 #pragma unroll
   for (int i = 0; i < T::FM; i++)
 #pragma unroll
-    for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_32x32x16<IN>(f.a[i], f.b[j], acc[i][j]);
+    for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_step<IN>(f.a[i], f.b[j], acc[i][j]);
 }
 
 // Interleave the LDS reads of the next k-step with the MFMAs of this one:
@@ -163,12 +163,14 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
     uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
-  using OA = OperandTile<T::BM, T::BK, LA, T::NT>;
-  using OB = OperandTile<T::BN, T::BK, LB, T::NT>;
-  using F = Frags<T, OA, OB>;
-  static_assert(T::KSTEPS % 2 == 0, "the register double buffer alternates two k-steps");
+  constexpr int ES = InT<IN>::ES;
+  constexpr int KSTEPS = T::BK / InT<IN>::KSTEP;          // MFMA k-steps per K tile
+  using OA = OperandTile<T::BM, T::BK, LA, T::NT, ES>;
+  using OB = OperandTile<T::BN, T::BK, LB, T::NT, ES>;
+  using F = Frags<T, IN>;
+  static_assert(KSTEPS % 2 == 0, "the register double buffer alternates two k-steps");
   constexpr int STAGE = OA::BYTES + OB::BYTES;
-  constexpr int READS = T::FM * (OA::kcontig ? 1 : 2) + T::FN * (OB::kcontig ? 1 : 2);
+  constexpr int READS = T::FM * frag_reads<OA, IN>() + T::FN * frag_reads<OB, IN>();
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -188,10 +190,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   const uint32_t a_voff = dma_lane_offset<OA>(tid, m0, M, lda, a_bytes, a_inner);
   const uint32_t b_voff = dma_lane_offset<OB>(tid, n0, N, ldb, b_bytes, b_inner);
   // Advance per load round (ROW_STEP rows) and per K tile, in bytes.
-  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * 2);
-  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * 2);
-  const uint32_t a_kstep = (uint32_t)(LA == KC ? 2 * T::BK : 2 * T::BK * lda);
-  const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
+  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * ES);
+  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * ES);
+  const uint32_t a_kstep = (uint32_t)(LA == KC ? ES * T::BK : ES * T::BK * lda);
+  const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
 
   auto issue = [&](int kt) {
     const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
@@ -220,19 +222,19 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     wait_dma();
     __syncthreads();                       // tile 0 is in stage 0
     if (KT > 1) issue(1);                  // tile 1 -> stage 1, lands during step 0
-    read_frags(cur, smem, smem + OA::BYTES, lane, wm, wn, 0);
+    read_frags<T, IN, OA, OB>(cur, smem, smem + OA::BYTES, lane, wm, wn, 0);
   }
 
   for (int kt = 0; kt < KT; ++kt) {
     const char *sA = smem + (kt & 1) * STAGE;
     const char *sB = sA + OA::BYTES;
 #pragma unroll
-    for (int kk = 0; kk + 1 < T::KSTEPS; kk += 2) {
-      read_frags(nxt, sA, sB, lane, wm, wn, kk + 1);
+    for (int kk = 0; kk + 1 < KSTEPS; kk += 2) {
+      read_frags<T, IN, OA, OB>(nxt, sA, sB, lane, wm, wn, kk + 1);
       mfma_block<T, IN>(acc, cur);
       interleave_reads_with_mfma<T::FM * T::FN, READS>();
-      if (kk + 2 < T::KSTEPS) {
-        read_frags(cur, sA, sB, lane, wm, wn, kk + 2);
+      if (kk + 2 < KSTEPS) {
+        read_frags<T, IN, OA, OB>(cur, sA, sB, lane, wm, wn, kk + 2);
         mfma_block<T, IN>(acc, nxt);
         interleave_reads_with_mfma<T::FM * T::FN, READS>();
       }
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
       wait_dma();
       __syncthreads();                     // tile kt+1 is in stage (kt+1)&1; stage kt&1 is free
       const char *nA = smem + ((kt + 1) & 1) * STAGE;
-      read_frags(cur, nA, nA + OA::BYTES, lane, wm, wn, 0);
+      read_frags<T, IN, OA, OB>(cur, nA, nA + OA::BYTES, lane, wm, wn, 0);
       if (kt + 2 < KT) issue(kt + 2);
     }
     mfma_block<T, IN>(acc, nxt);

@@ -63,11 +63,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
   constexpr int LOADERS = T::NT / 2;                     // group 0 issues every load
-  using OA = OperandTile<T::BM, T::BK, LA, LOADERS>;
-  using OB = OperandTile<T::BN, T::BK, LB, LOADERS>;
+  constexpr int ES = InT<IN>::ES;
+  constexpr int KSTEPS = T::BK / InT<IN>::KSTEP;          // MFMA k-steps per K tile
+  using OA = OperandTile<T::BM, T::BK, LA, LOADERS, ES>;
+  using OB = OperandTile<T::BN, T::BK, LB, LOADERS, ES>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int LOADS_PER_TILE = OA::LOADS + OB::LOADS;  // per group-0 wave
-  constexpr int FRAGS = T::KSTEPS * (T::FM + T::FN);      // fragment reads per memory phase
+  constexpr int FRAGS = KSTEPS * (T::FM + T::FN);         // fragment reads per memory phase
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -88,10 +90,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   int a_inner, b_inner;
   const uint32_t a_voff = dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, a_inner);
   const uint32_t b_voff = dma_lane_offset<OB>(tid & (LOADERS - 1), n0, N, ldb, b_bytes, b_inner);
-  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * 2);
-  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * 2);
-  const uint32_t a_kstep = (uint32_t)(LA == KC ? 2 * T::BK : 2 * T::BK * lda);
-  const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
+  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * ES);
+  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * ES);
+  const uint32_t a_kstep = (uint32_t)(LA == KC ? ES * T::BK : ES * T::BK * lda);
+  const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
   const int lwave = wave & 3;
 
   // Byte offsets of this wave's loads of K tile kt (round i of A is load i,
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     wg_barrier();                                        // b = 0
     if (group == 1) wg_barrier();                        // b = 1: group 1 idles through M(0) of group 0
 
-    v8i16 fa[T::KSTEPS][T::FM], fb[T::KSTEPS][T::FN];
+    typename InT<IN>::frag fa[KSTEPS][T::FM], fb[KSTEPS][T::FN];
     for (int kt = 0; kt < KT; ++kt) {
       // ---- memory phase M(kt)
       // Group 0 also starts the loads of tile kt+1 (their stage was freed at
@@ -158,13 +160,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
         uint32_t av = 0, bv = 0;
         if constexpr (LOAD) voffs(kt + 1, av, bv);
 #pragma unroll
-        for (int kk = 0; kk < T::KSTEPS; ++kk) {
+        for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
           for (int i = 0; i < T::FM + T::FN; i++) {
             if (i < T::FM)
-              fa[kk][i] = read_frag<OA>(sA, lane, wm * T::TM + 32 * i, kk);
+              fa[kk][i] = read_frag_in<OA, IN>(sA, lane, wm * T::TM + 32 * i, kk);
             else
-              fb[kk][i - T::FM] = read_frag<OB>(sB, lane, wn * T::TN + 32 * (i - T::FM), kk);
+              fb[kk][i - T::FM] = read_frag_in<OB, IN>(sB, lane, wn * T::TN + 32 * (i - T::FM), kk);
             if constexpr (LOAD) {
               // spread LOADS_PER_TILE loads evenly over the FRAGS fragment reads
               const int q = kk * (T::FM + T::FN) + i;
@@ -185,12 +187,12 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
       // ---- compute phase C(kt)
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kk = 0; kk < T::KSTEPS; ++kk)
+      for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
         for (int i = 0; i < T::FM; i++)
 #pragma unroll
           for (int j = 0; j < T::FN; j++)
-            acc[i][j] = mfma_32x32x16<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+            acc[i][j] = mfma_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
       __builtin_amdgcn_s_setprio(0);
       if (group == 0) {
         wait_dma();                                      // tile kt+1 landed

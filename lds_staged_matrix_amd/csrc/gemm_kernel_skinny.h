@@ -42,8 +42,7 @@ struct SkinnyTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, NS = NS_, GROUP_M = GROUP_M_;
   static constexpr int NT = 256, WAVES = 4;
   static constexpr int FM = BM / 32, FN = BN / 32;       // 32 x 32 accumulators per wave
-  static constexpr int KSTEPS = BK / 16 / WAVES;         // MFMA k-steps per wave per stage
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && KSTEPS >= 1, "split-K tile geometry");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "split-K tile geometry");
 };
 
 template <class T, int LA, int LB, int IN, int OUT>
@@ -51,8 +50,11 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_skinny_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
     uint32_t a_bytes, uint32_t b_bytes) {
-  using OA = OperandTile<T::BM, T::BK, LA, T::NT>;
-  using OB = OperandTile<T::BN, T::BK, LB, T::NT>;
+  constexpr int ES = InT<IN>::ES;
+  constexpr int KSTEPS = T::BK / InT<IN>::KSTEP / T::WAVES;   // MFMA k-steps per wave per stage
+  static_assert(KSTEPS >= 1 && KSTEPS * InT<IN>::KSTEP * T::WAVES == T::BK, "stage splits over the waves");
+  using OA = OperandTile<T::BM, T::BK, LA, T::NT, ES>;
+  using OB = OperandTile<T::BN, T::BK, LB, T::NT, ES>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int LPS = OA::LOADS + OB::LOADS;             // loads per thread per stage
   constexpr int L = T::NS - 1;                           // load lead, in stages
@@ -74,10 +76,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_skinny_kernel(
   int a_inner, b_inner;
   const uint32_t a_voff = dma_lane_offset<OA>(tid, m0, M, lda, a_bytes, a_inner);
   const uint32_t b_voff = dma_lane_offset<OB>(tid, n0, N, ldb, b_bytes, b_inner);
-  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * 2);
-  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * 2);
-  const uint32_t a_kstep = (uint32_t)(LA == KC ? 2 * T::BK : 2 * T::BK * lda);
-  const uint32_t b_kstep = (uint32_t)(LB == KC ? 2 * T::BK : 2 * T::BK * ldb);
+  const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * ES);
+  const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * ES);
+  const uint32_t a_kstep = (uint32_t)(LA == KC ? ES * T::BK : ES * T::BK * lda);
+  const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
   const int KT = (K + T::BK - 1) / T::BK;
 
   // Loads of stage kt into ring slot `slot`.  Stages past the end of K are
@@ -120,21 +122,21 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_skinny_kernel(
       issue(kt + L, ld_slot);
       const char *sA = smem + slot * STAGE;
       const char *sB = sA + OA::BYTES;
-      v8i16 fa[T::KSTEPS][T::FM], fb[T::KSTEPS][T::FN];
+      typename InT<IN>::frag fa[KSTEPS][T::FM], fb[KSTEPS][T::FN];
 #pragma unroll
-      for (int s = 0; s < T::KSTEPS; s++) {
-        const int kk = wave * T::KSTEPS + s;
+      for (int s = 0; s < KSTEPS; s++) {
+        const int kk = wave * KSTEPS + s;
 #pragma unroll
-        for (int i = 0; i < T::FM; i++) fa[s][i] = read_frag<OA>(sA, lane, 32 * i, kk);
+        for (int i = 0; i < T::FM; i++) fa[s][i] = read_frag_in<OA, IN>(sA, lane, 32 * i, kk);
 #pragma unroll
-        for (int j = 0; j < T::FN; j++) fb[s][j] = read_frag<OB>(sB, lane, 32 * j, kk);
+        for (int j = 0; j < T::FN; j++) fb[s][j] = read_frag_in<OB, IN>(sB, lane, 32 * j, kk);
       }
 #pragma unroll
-      for (int s = 0; s < T::KSTEPS; s++)
+      for (int s = 0; s < KSTEPS; s++)
 #pragma unroll
         for (int i = 0; i < T::FM; i++)
 #pragma unroll
-          for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_32x32x16<IN>(fa[s][i], fb[s][j], acc[i][j]);
+          for (int j = 0; j < T::FN; j++) acc[i][j] = mfma_step<IN>(fa[s][i], fb[s][j], acc[i][j]);
       slot = slot + 1 == T::NS ? 0 : slot + 1;
       ld_slot = ld_slot + 1 == T::NS ? 0 : ld_slot + 1;
     }

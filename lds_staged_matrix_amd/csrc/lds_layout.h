@@ -61,13 +61,18 @@ __host__ __device__ constexpr int kc_swizzle(int row, int row_bytes) {
                             : ((row / (256 / row_bytes)) & (row_bytes / 16 - 1));
 }
 
-// XOR applied to the chunk index of k-row `k` of an MN-contiguous tile: the
-// four k rows read by one 32-lane transposed-read phase land in four distinct
-// 64-byte quarters of the bank line.
-__host__ __device__ constexpr int mn_swizzle(int k, int row_bytes) {
+// XOR applied to the chunk index of k-row `k` of an MN-contiguous tile of
+// `es`-byte elements.  16-bit elements (ds_read_b64_tr_b16): one 32-lane
+// transposed-read phase reads 4 k-rows x 64 bytes, and the XOR puts the four
+// rows in four distinct 64-byte quarters of the bank line.  8-bit elements
+// (ds_read_b64_tr_b8): a phase reads 8 k-rows x 32 bytes, and the XOR puts
+// the eight rows in eight distinct 32-byte eighths of the bank line.
+__host__ __device__ constexpr int mn_swizzle(int k, int row_bytes, int es = 2) {
   return !LSM_LDS_SWIZZLE ? 0
-         : row_bytes >= 256 ? 4 * (k & 3)
-                            : (row_bytes == 128 ? 4 * ((k >> 1) & 1) : 0);
+         : es == 2 ? (row_bytes >= 256 ? 4 * (k & 3) : (row_bytes == 128 ? 4 * ((k >> 1) & 1) : 0))
+                   : (row_bytes >= 256 ? 2 * (k & 7)
+                                       : row_bytes == 128 ? 2 * ((k >> 1) & 3)
+                                                          : (row_bytes == 64 ? 2 * ((k >> 2) & 1) : 0));
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
@@ -76,8 +81,8 @@ __host__ __device__ constexpr int kc_chunk_offset(int row, int chunk, int row_by
 }
 
 // Byte offset of 16-byte chunk `chunk` of k-row `k` in an MN-contiguous tile.
-__host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_bytes) {
-  return k * row_bytes + 16 * (chunk ^ mn_swizzle(k, row_bytes));
+__host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_bytes, int es = 2) {
+  return k * row_bytes + 16 * (chunk ^ mn_swizzle(k, row_bytes, es));
 }
 
 // ---------------------------------------------------------------- loader
@@ -89,9 +94,9 @@ __host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_byte
 __host__ __device__ constexpr int loader_row(int id, int row_bytes) { return id / (row_bytes / 16); }
 __host__ __device__ constexpr int loader_chunk(int id, int row_bytes) { return id % (row_bytes / 16); }
 
-__host__ __device__ constexpr int loader_lds_offset(int id, int row_bytes, bool k_contig) {
+__host__ __device__ constexpr int loader_lds_offset(int id, int row_bytes, bool k_contig, int es = 2) {
   return k_contig ? kc_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes)
-                  : mn_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes);
+                  : mn_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes, es);
 }
 
 // ---------------------------------------------------------------- fragment reads
@@ -113,6 +118,31 @@ __host__ __device__ constexpr int frag_kc_offset(int lane, int base, int kk, int
 __host__ __device__ constexpr int frag_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
   return mn_chunk_offset(16 * kk + 8 * (lane >> 5) + 4 * h + ((lane >> 2) & 3),
                          (base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) / 8, row_bytes) +
+         8 * (lane & 1);
+}
+
+// Fragments of v_mfma_scale_f32_32x32x64_f8f6f4 on 8-bit elements (checked
+// with a probe): lane l holds operand row/column (l & 31) and 32 bytes; the
+// k of byte b only has to be the same for A and B, and here it is
+// k = 64*kk + 32*(l >> 5) + b.
+
+// K-contiguous 8-bit operand: two ds_read_b128 per fragment, q = 0, 1
+// delivering bytes 16q .. 16q + 15.
+__host__ __device__ constexpr int frag_kc8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return kc_chunk_offset(base + (lane & 31), 4 * kk + 2 * (lane >> 5) + q, row_bytes);
+}
+
+// MN-contiguous 8-bit operand: four ds_read_b64_tr_b8 per fragment, q = 0..3
+// delivering bytes 8q .. 8q + 7.  ds_read_b64_tr_b8 on gfx950 (measured with
+// a probe): inside each aligned group of 16 lanes, destination lane d
+// receives as byte j the byte (d & 7) of source lane (d >> 3) + 2j.  So
+// source lane s of group g (s' = s & 15) reads k-row
+// 64*kk + 32*(g >> 1) + 8q + (s' >> 1) at columns base + 16*(g & 1) +
+// 8*(s' & 1) .. +7, and destination lane l ends with column base + (l & 31),
+// k-rows 64*kk + 32*(l >> 5) + 8q + 0..7.
+__host__ __device__ constexpr int frag_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return mn_chunk_offset(64 * kk + 32 * (lane >> 5) + 8 * q + ((lane & 15) >> 1),
+                         (base + 16 * ((lane >> 4) & 1)) / 16, row_bytes, 1) +
          8 * (lane & 1);
 }
 

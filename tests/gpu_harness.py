@@ -18,12 +18,13 @@ import oracle
 import synth
 
 OUT_OF = {lsm.GEMM_BF16_F32: "f32", lsm.GEMM_BF16_BF16: "bf16", lsm.GEMM_F16_F16: "f16",
-          lsm.GEMM_F16_F32: "f32"}
+          lsm.GEMM_F16_F32: "f32", lsm.GEMM_E4M3_F32: "f32", lsm.GEMM_E4M3_BF16: "bf16"}
 IN_OF = {lsm.GEMM_BF16_F32: synth.BF16, lsm.GEMM_BF16_BF16: synth.BF16,
-         lsm.GEMM_F16_F16: synth.F16, lsm.GEMM_F16_F32: synth.F16}
+         lsm.GEMM_F16_F16: synth.F16, lsm.GEMM_F16_F32: synth.F16,
+         lsm.GEMM_E4M3_F32: synth.E4M3, lsm.GEMM_E4M3_BF16: synth.E4M3}
 LAYOUT = {"K": lsm.GEMM_K_CONTIG, "MN": lsm.GEMM_MN_CONTIG}
 OLAYOUT = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
-ODTYPE = {synth.BF16: oracle.BF16, synth.F16: oracle.F16}
+ODTYPE = {synth.BF16: oracle.BF16, synth.F16: oracle.F16, synth.E4M3: oracle.E4M3}
 CANARY_F32 = np.float32(-12345.5)
 CANARY_U16 = np.uint16(0x5A5A)
 
@@ -37,22 +38,26 @@ def handle():
     return _handle
 
 
-def ld_pad(extent, extra=0):
-    """Padding that makes the leading dimension a multiple of 8 elements."""
-    return (-max(extent, 1)) % 8 + 8 * extra
+def ld_pad(extent, extra=0, dtype=synth.BF16):
+    """Padding that makes the leading dimension a multiple of 16 bytes
+    (8 bf16/fp16 or 16 e4m3 elements)."""
+    q = 16 if dtype == synth.E4M3 else 8
+    return (-max(extent, 1)) % q + q * extra
 
 
 def problem(M, N, K, dtype, la, lb, dist, seeds=(1, 2), scale=1.0, extra_pad=0):
     inner_a = K if la == "K" else M
     inner_b = N if lb == "MN" else K
     return synth.make_problem(M, N, K, dtype, la, lb, dist, seeds[0], seeds[1], scale,
-                              pad_a=ld_pad(inner_a, extra_pad), pad_b=ld_pad(inner_b, extra_pad))
+                              pad_a=ld_pad(inner_a, extra_pad, dtype),
+                              pad_b=ld_pad(inner_b, extra_pad, dtype))
 
 
 def to_device(bits):
-    b = np.ascontiguousarray(bits).view(np.int16)
+    raw = np.ascontiguousarray(bits)
+    b = raw.view(np.int8) if raw.dtype == np.uint8 else raw.view(np.int16)
     if b.size == 0:
-        return torch.empty(8, dtype=torch.int16, device="cuda")
+        return torch.empty(16, dtype=torch.int16, device="cuda")
     return torch.from_numpy(b).to("cuda")
 
 

@@ -92,7 +92,11 @@ A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addr
     ((A0, B0, C0, 16, 16, -3, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
     ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 2, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
     ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, -1, 0), lsm.GEMM_ERR_INVALID_ARG),
-    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 4), lsm.GEMM_ERR_INVALID_ARG),
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 6), lsm.GEMM_ERR_INVALID_ARG),  # dtype
+    ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 4), lsm.GEMM_ERR_DEVICE),       # valid E4M3
+    ((A0, B0, C0, 16, 16, 24, 24, 16, 16, 0, 1, 4), lsm.GEMM_ERR_UNSUPPORTED),  # E4M3 lda 24 B
+    ((A0, B0, C0, 16, 16, 24, 32, 16, 16, 0, 1, 5), lsm.GEMM_ERR_UNSUPPORTED),  # E4M3 K % 16
+    ((A0, B0, C0, 16, 24, 32, 32, 32, 24, 0, 1, 4), lsm.GEMM_ERR_UNSUPPORTED),  # E4M3 N % 16
     ((A0, B0, C0, 0, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_OK),               # empty: no-op
     ((A0, B0, C0, 16, 0, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_OK),
     ((A0, B0, 0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),   # NULL C
