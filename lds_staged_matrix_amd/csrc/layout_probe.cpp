@@ -21,4 +21,13 @@ int lsm_frag_kc_offset(int lane, int base, int kk, int row_bytes) {
 int lsm_frag_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
   return lsm::frag_tr_offset(lane, base, kk, h, row_bytes);
 }
+int lsm_loader_lds_offset8(int id, int row_bytes, int k_contig) {
+  return lsm::loader_lds_offset(id, row_bytes, k_contig != 0, 1);
+}
+int lsm_frag_kc8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return lsm::frag_kc8_offset(lane, base, kk, q, row_bytes);
+}
+int lsm_frag_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return lsm::frag_tr8_offset(lane, base, kk, q, row_bytes);
+}
 }

@@ -112,7 +112,8 @@ def layouts():
     for s, p in paths.items():
         lib = ctypes.CDLL(p)
         for f in ("lsm_kc_chunk_offset", "lsm_mn_chunk_offset", "lsm_loader_lds_offset",
-                  "lsm_frag_kc_offset", "lsm_frag_tr_offset", "lsm_layout_swizzled"):
+                  "lsm_frag_kc_offset", "lsm_frag_tr_offset", "lsm_layout_swizzled",
+                  "lsm_loader_lds_offset8", "lsm_frag_kc8_offset", "lsm_frag_tr8_offset"):
             getattr(lib, f).restype = ctypes.c_int
         libs["swizzled" if s == "" else "linear"] = lib
     assert libs["swizzled"].lsm_layout_swizzled() == 1
@@ -188,6 +189,58 @@ def test_register_staged_writes_are_conflict_free(layouts, row_bytes, kc):
     for w in range(8):
         addrs = [lib.lsm_loader_lds_offset(64 * w + l, row_bytes, int(kc)) for l in range(64)]
         assert degree(addrs, 16) == 1
+
+
+# 8-bit (E4M3) tiles.  K-contiguous rows hold BK bytes and are read with two
+# ds_read_b128 per fragment; MN-contiguous rows hold the tile width in bytes
+# and are read with four ds_read_b64_tr_b8 (8 bytes per lane, 32-lane
+# phases of 8 k-rows x 32 bytes).
+def kc8_read_degree(lib, row_bytes, rows):
+    worst = 1
+    for base in range(0, rows, 32):
+        for kk in range(row_bytes // 64):
+            for q in range(2):
+                addrs = [lib.lsm_frag_kc8_offset(l, base, kk, q, row_bytes) for l in range(64)]
+                worst = max(worst, degree(addrs, 16))
+    return worst
+
+
+def tr8_read_degree(lib, row_bytes, krows):
+    worst = 1
+    for base in range(0, row_bytes, 32):
+        for kk in range(krows // 64):
+            for q in range(4):
+                addrs = [lib.lsm_frag_tr8_offset(l, base, kk, q, row_bytes) for l in range(64)]
+                worst = max(worst, degree(addrs, 8))
+    return worst
+
+
+@pytest.mark.parametrize("row_bytes,rows", [(128, 256), (128, 64), (256, 32)])
+def test_swizzled_fp8_k_contig_reads_are_conflict_free(layouts, row_bytes, rows):
+    assert kc8_read_degree(layouts["swizzled"], row_bytes, rows) == 1
+
+
+@pytest.mark.parametrize("row_bytes,krows", [(256, 128), (128, 128), (64, 128), (64, 256), (32, 256)])
+def test_swizzled_fp8_transposed_reads_are_conflict_free(layouts, row_bytes, krows):
+    assert tr8_read_degree(layouts["swizzled"], row_bytes, krows) == 1
+
+
+@pytest.mark.parametrize("row_bytes,want", [(256, 8), (128, 4), (64, 2), (32, 1)])
+def test_unswizzled_fp8_transposed_reads_conflict(layouts, row_bytes, want):
+    # 8 k-rows x 32 bytes per phase: rows of 256 bytes or more all start at one
+    # bank (8-way); 128-byte rows pair up (4-way), 64-byte rows fill half a
+    # line (2-way), 32-byte rows fill one line
+    assert tr8_read_degree(layouts["linear"], row_bytes, 128) == want
+
+
+@pytest.mark.parametrize("row_bytes,kc", [(128, True), (256, True), (256, False), (128, False),
+                                          (64, False)])
+def test_fp8_loader_slots_are_a_permutation(layouts, row_bytes, kc):
+    # every 16-byte chunk of a tile gets exactly one LDS slot
+    lib = layouts["swizzled"]
+    n = 4096 // 16
+    slots = sorted(lib.lsm_loader_lds_offset8(i, row_bytes, int(kc)) for i in range(n))
+    assert slots == [16 * i for i in range(n)]
 
 
 def test_direct_to_lds_writes_are_conflict_free():
