@@ -107,6 +107,10 @@ __device__ __forceinline__ v16f32 mfma_step(typename InT<IN>::frag a, typename I
     return mfma_32x32x16<IN>(a, b, c);
 }
 
+// Keeps an accumulator's MFMAs ahead of this point: the compiler may otherwise
+// sink register-only MFMAs past a following barrier into the next phase.
+__device__ __forceinline__ void pin_acc(v16f32 &c) { asm volatile("" : "+v"(c)); }
+
 // One 32x32x16 operand fragment: lane l gets row/column (l & 31) of the
 // fragment starting at `base`, k = 16*kk + 8*(l >> 5) + 0..7.
 // One 32 x 64 operand fragment of 8-bit elements (k-step kk of the tile).

@@ -239,7 +239,15 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
         interleave_reads_with_mfma<T::FM * T::FN, READS>();
       }
     }
-    // `nxt` holds the last k-step of this stage (KSTEPS is even).
+    // `nxt` holds the last k-step of this stage (KSTEPS is even).  The MFMAs
+    // issued so far run while this wave waits for the next tile (with two
+    // k-steps per tile the compiler would otherwise sink them past the wait).
+    if constexpr (KSTEPS == 2) {
+#pragma unroll
+      for (int i = 0; i < T::FM; i++)
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) pin_acc(acc[i][j]);
+    }
     if (kt + 1 < KT) {
       wait_dma();
       __syncthreads();                     // tile kt+1 is in stage (kt+1)&1; stage kt&1 is free

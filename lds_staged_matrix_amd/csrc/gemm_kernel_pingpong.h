@@ -193,6 +193,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
 #pragma unroll
           for (int j = 0; j < T::FN; j++)
             acc[i][j] = mfma_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < T::FM; i++)
+#pragma unroll
+        for (int j = 0; j < T::FN; j++) pin_acc(acc[i][j]);
       __builtin_amdgcn_s_setprio(0);
       if (group == 0) {
         wait_dma();                                      // tile kt+1 landed
