@@ -115,3 +115,23 @@ def test_fp8_unsupported_extents_rejected_untouched():
     assert run(16, 16, 32, 40, 16, 0, 1) == lsm.GEMM_ERR_UNSUPPORTED   # lda not 16 bytes
     torch.cuda.synchronize()
     assert bool(torch.all(C == 7.0))
+
+
+def test_fp8_footprint_beyond_2gib_rejected_untouched():
+    # fp8 runs only on the direct-to-LDS kernels, whose buffer offsets are
+    # 32-bit: an A footprint past 2^31 bytes is GEMM_ERR_UNSUPPORTED, with
+    # nothing enqueued and C untouched.
+    h = H.handle()
+    M, N, K = 72, 64, 64
+    lda = 1 << 25                           # 71 rows of 32 MiB: 2.2 GiB footprint
+    assert ((M - 1) * lda + K) > (1 << 31)
+    A = torch.zeros((M - 1) * lda + K, dtype=torch.int8, device="cuda")
+    B = torch.zeros(K * N, dtype=torch.int8, device="cuda")
+    C = torch.full((M * N,), 7.0, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    st = lsm.gemm_run(h, A, B, C, M, N, K, lda, N, N, lsm.GEMM_K_CONTIG, lsm.GEMM_MN_CONTIG,
+                      lsm.GEMM_E4M3_F32, s)
+    assert st == lsm.GEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool(torch.all(C == 7.0))
+    del A

@@ -275,6 +275,24 @@ def test_config_skinny_integer_exact():
 
 # ------------------------------------------------------------------ ABI behaviour on the GPU
 
+@pytest.mark.parametrize("big", ["A", "B"])
+def test_operand_footprint_beyond_2gib(big):
+    # An operand whose footprint passes 2^31 bytes (72 rows of a 2^24 + 72
+    # element leading dimension, 2.4 GB) is beyond the 32-bit buffer offsets
+    # of the direct-to-LDS kernels: the register-staged kernel with 64-bit
+    # addressing takes it, bit-exact against the oracle.
+    M, N, K = 72, 200, 72
+    wide = (1 << 24) + 72 - K if big == "A" else (1 << 24) + 72 - N
+    announce("footprint > 2 GiB", big, M, N, K)
+    p = synth.make_problem(M, N, K, synth.BF16, "K", "MN", "int", 31, 32,
+                           pad_a=wide if big == "A" else 0, pad_b=wide if big == "B" else 0)
+    fp = (((M - 1) * p.lda + K) if big == "A" else ((K - 1) * p.ldb + N)) * 2
+    assert fp > (1 << 31)
+    C = H.run_gpu(p, lsm.GEMM_BF16_F32, ldc=N + 8, extra_rows=1)
+    H.assert_canary(C, M, N, lsm.GEMM_BF16_F32)
+    H.assert_exact(C[:M, :N], H.oracle_full(p), lsm.GEMM_BF16_F32, f"footprint {big}")
+
+
 def test_error_paths_leave_c_untouched():
     announce("errors")
     h = H.handle()
