@@ -113,8 +113,11 @@ def cpu_baseline(p, rows):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 500 untimed and 100 timed launches, the ladder page's test configuration
+    # ("An educational GEMM ladder for Helios GPUs", Test Configuration); the
+    # chip needs ~80 ms of load before its clock settles.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layout", default=None, help="e.g. K,MN (A contiguity, B contiguity)")
     ap.add_argument("--cpu-rows", type=int, default=None,
