@@ -129,13 +129,12 @@ def main():
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
                          "(noswizzle, scalar_tr, ring2) instead of the library")
-    ap.add_argument("--flushed", action="store_true",
-                    help="also time 20 launches with the caches flushed before each "
-                         "(always done for HBM-bound workloads)")
+    ap.add_argument("--no-flushed", action="store_true",
+                    help="skip the 20 launches timed with the caches flushed before each")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build is a single-GPU kernel library "
+        print("bench.py measures one GPU only: this is a single-GPU kernel library "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -211,7 +210,7 @@ def main():
     # hold none of A, B or C.  The flush reads (a write would leave dirty
     # lines whose write-back competes with the timed kernel).
     fl_ms = []
-    do_flush = args.flushed or hbm_bound
+    do_flush = not args.no_flushed
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if do_flush else None
     for i in range(20 if do_flush else 0):
         flush.sum()

@@ -1,0 +1,59 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the readers of the
+committed rocprofv3 summaries, and the oracle CPU-baseline leg."""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_source_hash_is_stable():
+    h = bench.kernel_source_hash()
+    assert re.fullmatch(r"[0-9a-f]{16}", h)
+    assert h == bench.kernel_source_hash()
+
+
+def _recorded_hash(name):
+    text = open(os.path.join(ROOT, "profiles", name)).read()
+    return re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M).group(1)
+
+
+@pytest.mark.parametrize("workload", ["bf16_8192_nn_f32", "e4m3_8192_nn_f32",
+                                      "bf16_skinny_32x16384x8192_nn_bf16"])
+def test_traffic_is_read_only_for_the_profiled_sources(workload):
+    rec = _recorded_hash(f"hbm_traffic_{workload}.txt")
+    got = bench.read_traffic(workload, rec)
+    assert got is not None and got > 0
+    assert bench.read_traffic(workload, "0" * 16) is None
+    assert bench.read_traffic("no_such_workload", rec) is None
+
+
+def test_conflict_rate_is_read_only_for_the_profiled_sources():
+    rec = _recorded_hash("lds_bank_conflicts_all_workloads.txt")
+    for wl, lay in [("bf16_8192_nn_f32", "NN"), ("bf16_4096_all_bf16", "NT")]:
+        v = bench.read_conflict_rate(wl, lay, rec)
+        assert v is not None and 0.0 <= v < 0.05
+        assert bench.read_conflict_rate(wl, lay, "0" * 16) is None
+
+
+def test_cpu_baseline_times_the_oracle_on_a_sample():
+    p = synth.make_problem(48, 40, 32, synth.BF16, "K", "MN", "uniform", 1, 2)
+    r = bench.cpu_baseline(p, 8)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "rows 0..7" in r["sample"]
