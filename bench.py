@@ -42,14 +42,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """Source text without comments and blank-line or indentation changes,
+    so that editing a comment does not change the kernels' identity."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(l.split()) for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash():
+    """Identity of the kernel sources that the committed profiles were taken on."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, KERNEL_DIR)
     for name in sorted(os.listdir(d)):
         if name.endswith((".h", ".hip")):
             h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(d, name), encoding="utf-8") as f:
+                h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

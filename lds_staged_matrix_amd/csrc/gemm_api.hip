@@ -1,6 +1,10 @@
 // gemm_api.hip -- the C ABI declared in include/lds_gemm.h: argument
-// validation, choice of tile shape, and the kernel launch on the caller's
-// stream.  Every launched kernel comes from gemm_kernel.h.
+// validation, choice of kernel and tile shape, and the launch on the
+// caller's stream.  The kernels: the ping-pong kernel (gemm_kernel_pingpong.h,
+// shapes with at least 256 tiles of 256 x 256), the direct-to-LDS kernel
+// (gemm_kernel_dma.h, 128 and 64 tiles), the split-K ring kernel
+// (gemm_kernel_skinny.h, M <= 32) and the register-staged kernel
+// (gemm_kernel.h, shapes the 16-byte direct-to-LDS loads cannot take).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
