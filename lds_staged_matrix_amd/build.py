@@ -27,6 +27,7 @@ VARIANTS = {
     "noswizzle": ["-DLSM_LDS_SWIZZLE=0"],   # row-major LDS tiles, no XOR swizzle
     "scalar_tr": ["-DLSM_TR_READ=0"],       # 8 x 16-bit LDS reads instead of ds_read_b64_tr_b16
     "ring2": ["-DLSM_RING_STAGES=2"],       # M <= 32 kernel with a 2-stage instead of 6-stage ring
+    "noxcd": ["-DLSM_XCD_REMAP=0"],         # tiles in hardware workgroup order, not grouped per XCD
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

@@ -30,4 +30,8 @@ int lsm_frag_kc8_offset(int lane, int base, int kk, int q, int row_bytes) {
 int lsm_frag_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
   return lsm::frag_tr8_offset(lane, base, kk, q, row_bytes);
 }
+int lsm_xcd_logical_id(int bid, int nwg) { return lsm::xcd_logical_id(bid, nwg); }
+void lsm_tile_coords(int lid, int tiles_m, int tiles_n, int group_m, int *tm, int *tn) {
+  lsm::tile_coords(lid, tiles_m, tiles_n, group_m, *tm, *tn);
+}
 }

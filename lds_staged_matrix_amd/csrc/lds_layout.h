@@ -152,8 +152,17 @@ __host__ __device__ constexpr int frag_tr8_offset(int lane, int base, int kk, in
 // and each XCD has its own L2.  The logical tile id gives each XCD one
 // contiguous range of ids, then walks tiles in groups of `group_m` tile rows
 // so the workgroups resident on one XCD at a time share A and B panels.
+// LSM_XCD_REMAP=0 (an A/B build only) keeps the hardware order instead.
+#ifndef LSM_XCD_REMAP
+#define LSM_XCD_REMAP 1
+#endif
 __host__ __device__ constexpr int xcd_logical_id(int bid, int nwg) {
+#if LSM_XCD_REMAP
   return (bid & 7) * (nwg >> 3) + ((bid & 7) < (nwg & 7) ? (bid & 7) : (nwg & 7)) + (bid >> 3);
+#else
+  (void)nwg;
+  return bid;
+#endif
 }
 
 __host__ __device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, int group_m,
