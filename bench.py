@@ -137,7 +137,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
-                         "(noswizzle, scalar_tr, ring2, noxcd) instead of the library")
+                         "(noswizzle, scalar_tr, ring2, noxcd, stage1) instead of the library")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the 20 launches timed with the caches flushed before each")
     args = ap.parse_args()

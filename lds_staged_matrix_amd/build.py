@@ -28,6 +28,7 @@ VARIANTS = {
     "scalar_tr": ["-DLSM_TR_READ=0"],       # 8 x 16-bit LDS reads instead of ds_read_b64_tr_b16
     "ring2": ["-DLSM_RING_STAGES=2"],       # M <= 32 kernel with a 2-stage instead of 6-stage ring
     "noxcd": ["-DLSM_XCD_REMAP=0"],         # tiles in hardware workgroup order, not grouped per XCD
+    "stage1": ["-DLSM_DMA_STAGES=1"],       # 128/64 direct-to-LDS kernel with one LDS stage, no overlap
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

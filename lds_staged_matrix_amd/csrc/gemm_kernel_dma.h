@@ -158,6 +158,14 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
   }
 }
 
+// LSM_DMA_STAGES = 1 builds this kernel with a single LDS stage: every K
+// tile is loaded, waited for and only then computed, with no overlap of the
+// loads and the MFMAs.  It exists only for the A/B build that measures what
+// the double-buffered pipeline buys; the library is built with 2.
+#ifndef LSM_DMA_STAGES
+#define LSM_DMA_STAGES 2
+#endif
+
 template <class T, int LA, int LB, int IN, int OUT>
 __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
@@ -170,8 +178,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   using F = Frags<T, IN>;
   static_assert(KSTEPS % 2 == 0, "the register double buffer alternates two k-steps");
   constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int STAGES = LSM_DMA_STAGES;
+  static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
   constexpr int READS = T::FM * frag_reads<OA, IN>() + T::FN * frag_reads<OB, IN>();
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
 
   auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
+    const uint32_t st = lds0 + (uint32_t)((STAGES == 1 ? 0 : kt & 1) * STAGE);
     const int k0 = kt * T::BK;
     uint32_t av = a_voff, bv = b_voff;
     if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
@@ -217,6 +227,25 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
 
   const int KT = (K + T::BK - 1) / T::BK;
   F cur, nxt;
+  if constexpr (STAGES == 1) {
+    // Load, wait, compute, in turn: the loads of tile kt+1 start only when
+    // every wave has read tile kt.
+    if (KT > 0) issue(0);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_dma();
+      __syncthreads();                     // tile kt is in the stage
+      read_frags<T, IN, OA, OB>(cur, smem, smem + OA::BYTES, lane, wm, wn, 0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < KSTEPS; kk += 2) {
+        read_frags<T, IN, OA, OB>(nxt, smem, smem + OA::BYTES, lane, wm, wn, kk + 1);
+        mfma_block<T, IN>(acc, cur);
+        if (kk + 2 < KSTEPS) read_frags<T, IN, OA, OB>(cur, smem, smem + OA::BYTES, lane, wm, wn, kk + 2);
+        mfma_block<T, IN>(acc, nxt);
+      }
+      __syncthreads();                     // every wave is done with the stage
+      if (kt + 1 < KT) issue(kt + 1);
+    }
+  } else {
   if (KT > 0) {
     issue(0);
     wait_dma();
@@ -257,11 +286,12 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     }
     mfma_block<T, IN>(acc, nxt);
   }
+  }
 
   if constexpr (T::TN == 64) {
     if (c_vec) {
       __syncthreads();                     // every wave is past its last LDS read
-      epilogue_lds<T, OUT, 2 * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+      epilogue_lds<T, OUT, STAGES * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
       return;
     }
   }

@@ -1,6 +1,7 @@
 """The A/B builds (one design choice changed each: no LDS swizzle, scalar
 16-bit reads instead of ds_read_b64_tr_b16, a 2-stage ring for M <= 32,
-tiles in hardware workgroup order instead of the per-XCD order)
+tiles in hardware workgroup order instead of the per-XCD order, one LDS
+stage instead of two in the direct-to-LDS kernel)
 compute the same products: bit-identical to the library on integer-valued
 inputs, whose result is unique.  Their speed and counters are what the
 benchmark compares; this checks that they are the same computation."""
@@ -14,7 +15,7 @@ import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd"]
+VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1"]
 # one shape per kernel: ping-pong (>= 256 tiles of 256), 128 x 128 tile
 # (>= 256 tiles of 128), 64 x 64 tile, split-K ring (M <= 32)
 SHAPES = [(4096, 4096, 136), (2048, 2056, 200), (520, 264, 1000), (32, 1000, 1032)]
