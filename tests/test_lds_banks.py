@@ -180,6 +180,25 @@ def test_unswizzled_transposed_reads_conflict(layouts, row_bytes, want):
     assert tr_read_degree(layouts["linear"], row_bytes, 32) == want
 
 
+# the tile rows the kernels use: K-contiguous BK of 32..128 (16-bit) or 64..256
+# (8-bit) elements, MN-contiguous widths of 32..256 (16-bit) or 64..512 (8-bit)
+@pytest.mark.parametrize("row_bytes,kc", [(64, True), (128, True), (256, True),
+                                          (64, False), (128, False), (256, False), (512, False)])
+@pytest.mark.parametrize("es", [2, 1])
+def test_swizzle_repeats_every_direct_to_lds_load_round(layouts, row_bytes, kc, es):
+    # The direct-to-LDS loads write lane-linear 1 KiB blocks, and every lane
+    # keeps one global offset for all its load rounds (256 loader threads,
+    # 256*16 bytes = 4096 / row_bytes rows per round).  That is only right if
+    # the LDS image of round i is round 0's shifted by 4 KiB, i.e. the swizzle
+    # repeats every round; a swizzle with a longer period in the row index
+    # would put the later rounds' chunks in the wrong places.
+    lib = layouts["swizzled"]
+    off = lib.lsm_loader_lds_offset if es == 2 else lib.lsm_loader_lds_offset8
+    for i in range(1, 4):
+        for tid in range(256):
+            assert off(tid + 256 * i, row_bytes, int(kc)) == off(tid, row_bytes, int(kc)) + 4096 * i
+
+
 @pytest.mark.parametrize("row_bytes,kc", [(64, True), (128, True), (256, True), (512, False),
                                           (256, False), (128, False), (64, False)])
 def test_register_staged_writes_are_conflict_free(layouts, row_bytes, kc):
