@@ -181,6 +181,32 @@ def test_lds_staged_epilogue_edges_integer_exact(shape, gdtype):
         H.assert_exact(C[rows, cols], H.oracle_entries(p, rows, cols), gdtype, "entries")
 
 
+@pytest.mark.parametrize("shape", [(4100, 4104, 136), (2050, 2056, 264)])
+def test_c_base_not_16_byte_aligned(shape):
+    # C two bytes past a 16-byte boundary (bf16 out, ldc a multiple of 8):
+    # the 16-byte LDS-staged stores are off, the per-element epilogue runs;
+    # nothing is written before C or outside the M x N block.
+    M, N, K = shape
+    announce("C base + 2 bytes", M, N, K)
+    p = H.problem(M, N, K, synth.BF16, "K", "MN", "int", (121, 122))
+    A, B = H.to_device(p.A), H.to_device(p.B)
+    ldc = N + 8
+    buf = torch.full((M * ldc + 16,), int(H.CANARY_U16), dtype=torch.int16, device="cuda")
+    st = lsm.gemm_run(H.handle(), A, B, buf.data_ptr() + 2, M, N, K, p.lda, p.ldb, ldc,
+                      H.LAYOUT["K"], H.LAYOUT["MN"], lsm.GEMM_BF16_BF16, torch.cuda.current_stream())
+    assert st == lsm.GEMM_OK
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy().view(np.uint16)
+    assert host[0] == H.CANARY_U16
+    C = host[1:1 + M * ldc].reshape(M, ldc)
+    H.assert_canary(C, M, N, lsm.GEMM_BF16_BF16)
+    rng = np.random.default_rng(2)
+    for r0, r1 in ((0, 2), (M - 2, M)):
+        H.assert_exact(C[r0:r1, :N], H.oracle_rows(p, r0, r1), lsm.GEMM_BF16_BF16, f"rows {r0}")
+    rows, cols = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
+    H.assert_exact(C[rows, cols], H.oracle_entries(p, rows, cols), lsm.GEMM_BF16_BF16, "entries")
+
+
 def sample_check(p, C, gdtype, exact, rows_sel, n_entries=4000, seed=0):
     rng = np.random.default_rng(seed)
     for r0, r1 in rows_sel:
