@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
                          "(noswizzle, scalar_tr, ring2, noxcd, stage1) instead of the library")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the 20 launches timed with the caches flushed before each")
     args = ap.parse_args()
@@ -230,6 +232,31 @@ def main():
         torch.cuda.synchronize()
         fl_ms.append(s.elapsed_time(e))
     del flush
+
+    # The same K steps captured in one HIP graph and replayed: the per-step
+    # time without host launch overhead, what a captured loop of GEMMs gets
+    # (gemm_run only enqueues kernels, so it can be captured).
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(g, stream=side):
+            cs = torch.cuda.current_stream()
+            for _ in range(args.steps):
+                st = lib.gemm_run(h, A, B, C, M, N, K, p.lda, p.ldb, N, la, lb, gd, cs)
+                if st != lsm.GEMM_OK:
+                    raise lsm.GemmError(st, "gemm_run (graph capture)")
+        stream.wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        g.replay()
+        e0.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = s0.elapsed_time(e0) / args.steps
+        del g
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     kavg = float(kern_ms.mean())
@@ -247,7 +274,8 @@ def main():
 
     log(f"kernel ms: mean {kavg:.4f} median {np.median(kern_ms):.4f} min {kern_ms.min():.4f}; "
         f"flushed-cache median {np.median(fl_ms) if fl_ms else float('nan'):.4f} ms; "
-        f"wall per step {ms_per_step:.4f} ms")
+        f"wall per step {ms_per_step:.4f} ms; graph replay per step "
+        f"{graph_ms if graph_ms is not None else float('nan'):.4f} ms")
     log(f"kernel TFLOP/s {flops / (kavg * 1e-3) / 1e12:.1f}, "
         f"{flops / (kavg * 1e-3) / 1e12 / peak_tflops * 100:.1f}% of the dense "
         f"{'fp8' if in_bytes == 1 else 'bf16'} peak; "
@@ -275,6 +303,7 @@ def main():
                    "inputs": f"{w['dist']} x{w['scale']} seeds {w['seeds']}",
                    "kernel_ms_mean": round(kavg, 5), "kernel_ms_flushed_median":
                        round(float(np.median(fl_ms)), 5) if fl_ms else None,
+                   "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
                    "kernel_source_hash": src_hash},
         "roofline": roof,
         "cpu_baseline": cpu,

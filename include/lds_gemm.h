@@ -28,7 +28,9 @@
  * handle's device) and keeps them alive until the work queued on `stream`
  * has finished.  The library never allocates, frees or retains caller
  * memory and allocates no workspace.  gemm_run only enqueues work on
- * `stream` and returns without synchronising the host.
+ * `stream` and returns without synchronising the host; it launches kernels
+ * and nothing else (no allocation, memset or copy), so a call made while
+ * `stream` is being captured into a HIP graph is captured and replays.
  *
  * Errors: every function returns a gemm_status.  Arguments are validated
  * before anything is launched; on an error nothing is enqueued and C is
