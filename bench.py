@@ -91,14 +91,22 @@ def read_conflict_rate(workload, layout_name, src_hash):
     return float(m.group(1))
 
 
-def make_inputs(w, layout):
+def make_inputs(w, layout, inputs="workload"):
+    """The workload's seeded operands.  `inputs` = "int" draws integers
+    -2..2 instead; "zeros" / "ones" overwrite the device copies with that
+    constant (diagnostics of the data-dependent clock only)."""
     import torch
     la, lb = layout
-    p = synth.make_problem(w["M"], w["N"], w["K"], w["dtype"], la, lb, w["dist"], w["seeds"][0],
-                           w["seeds"][1], w["scale"])
+    dist = "int" if inputs == "int" else w["dist"]
+    p = synth.make_problem(w["M"], w["N"], w["K"], w["dtype"], la, lb, dist, w["seeds"][0],
+                           w["seeds"][1], 1.0 if inputs == "int" else w["scale"])
     raw = (lambda x: x.view(np.int8)) if w["dtype"] == synth.E4M3 else (lambda x: x.view(np.int16))
     A = torch.from_numpy(raw(p.A)).cuda()
     B = torch.from_numpy(raw(p.B)).cuda()
+    if inputs in ("zeros", "ones"):
+        one = {synth.BF16: 0x3F80, synth.F16: 0x3C00, synth.E4M3: 0x38}[w["dtype"]]
+        for t in (A, B):
+            t.fill_(0 if inputs == "zeros" else one)
     return p, A, B
 
 
@@ -138,6 +146,9 @@ def main():
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
                          "(noswizzle, scalar_tr, ring2, noxcd, stage1) instead of the library")
+    ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
+                    help="operand values: the workload's (default), or integers -2..2, all "
+                         "zeros or all ones to show how the clock depends on the data")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
@@ -169,7 +180,7 @@ def main():
     gd = DTYPE_CODE[(w["dtype"], w["out"])]
     M, N, K = w["M"], w["N"], w["K"]
     log(f"workload {args.workload} layout {layout} M={M} N={N} K={K}")
-    p, A, B = make_inputs(w, layout)
+    p, A, B = make_inputs(w, layout, args.inputs)
     C = torch.empty(M * N, dtype=torch.float32 if w["out"] == "f32" else torch.int16,
                     device="cuda")
     lib = lsm.ablation_library(args.variant) if args.variant else lsm
@@ -300,7 +311,8 @@ def main():
                                f"fp32 accumulation", "name": args.workload,
                    "M": M, "N": N, "K": K, "layout": "".join("N" if x == ("K" if i == 0 else "MN")
                                                           else "T" for i, x in enumerate(layout)),
-                   "inputs": f"{w['dist']} x{w['scale']} seeds {w['seeds']}",
+                   "inputs": f"{w['dist']} x{w['scale']} seeds {w['seeds']}" if args.inputs == "workload"
+                             else f"{args.inputs} (diagnostic, not the workload's values)",
                    "kernel_ms_mean": round(kavg, 5), "kernel_ms_flushed_median":
                        round(float(np.median(fl_ms)), 5) if fl_ms else None,
                    "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
