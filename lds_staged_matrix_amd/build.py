@@ -81,11 +81,11 @@ def build_layout_host(verbose: bool = False):
 
 
 def build_all(verbose: bool = False):
-    """Every build, four hipcc processes at a time."""
+    """Every build, six hipcc processes at a time."""
     from concurrent.futures import ThreadPoolExecutor
     jobs = [lambda: build(verbose)] + [lambda n=n: build(verbose, variant=n) for n in VARIANTS] + \
            [lambda: build_layout_host(verbose)]
-    with ThreadPoolExecutor(max_workers=4) as pool:
+    with ThreadPoolExecutor(max_workers=6) as pool:
         for f in [pool.submit(j) for j in jobs]:
             f.result()
 
