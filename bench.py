@@ -127,6 +127,46 @@ def cpu_baseline(p, rows):
                       f"{p.M}x{p.N}x{p.K} problem ({rows * p.N} outputs), {dt:.2f} s wall"}
 
 
+def vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p, steps, warmup, stream):
+    """Same operands, same launch counts: torch.matmul (hipBLASLt) against
+    this library, both with bf16 output, for 16-bit inputs with A
+    K-contiguous and B N-contiguous (row-major A[M,K] @ B[K,N]).  A reference
+    point only; nothing in the library calls torch."""
+    import torch
+    if w["dtype"] == synth.E4M3 or tuple(layout) != ("K", "MN") or p.lda != K or p.ldb != N:
+        return None
+    tdt = torch.bfloat16 if w["dtype"] == synth.BF16 else torch.float16
+    gd = DTYPE_CODE[(w["dtype"], "bf16" if w["dtype"] == synth.BF16 else "f16")]
+    At, Bt = A.view(tdt).view(M, K), B.view(tdt).view(K, N)
+    Ct = torch.empty(M, N, dtype=tdt, device="cuda")
+
+    def ours():
+        lib.gemm_run(h, A, B, Ct, M, N, K, p.lda, p.ldb, N, 0, 1, gd, stream)
+
+    def theirs():
+        torch.matmul(At, Bt, out=Ct)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(steps):
+            fn()
+        e0.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) / steps
+
+    res = {}
+    for name, fn in (("hipblaslt", theirs), ("library", ours), ("hipblaslt_again", theirs)):
+        ms = timed(fn)
+        res[name + "_ms"] = round(ms, 5)
+        res[name + "_tflops"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
+    res["output"] = "bf16" if w["dtype"] == synth.BF16 else "f16"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +189,9 @@ def main():
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) and this library with 16-bit "
+                         "output on the same operands (A K-contiguous, B N-contiguous only)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
@@ -325,6 +368,9 @@ def main():
     if args.variant:
         line["config"]["ablation_build"] = args.variant
         roof["traffic"] = None
+    if args.vs_hipblaslt:
+        line["config"]["vs_hipblaslt"] = vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p,
+                                                      args.steps, args.warmup, stream)
     lib.gemm_destroy(h)
     print(json.dumps(line), flush=True)
 
