@@ -76,10 +76,13 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
 // The compiler reserves M0 and warns when asm clobbers it.  In these kernels
 // no compiler-generated instruction reads M0 (gfx950 LDS instructions do not
 // use it), and every asm statement sets M0 right before the load that uses it.
+// A scalar write of M0 needs one wait state before an LDS-DMA load reads it
+// (the compiler inserts the same s_nop for its own buffer-load-to-LDS
+// builtin on gfx9-family targets); its hazard check does not look inside asm.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_block, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_block), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory", "m0");
