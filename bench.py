@@ -128,23 +128,41 @@ def cpu_baseline(p, rows):
 
 
 def vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p, steps, warmup, stream):
-    """Same operands, same launch counts: torch.matmul (hipBLASLt) against
-    this library, both with bf16 output, for 16-bit inputs with A
-    K-contiguous and B N-contiguous (row-major A[M,K] @ B[K,N]).  A reference
-    point only; nothing in the library calls torch."""
+    """Same operands, same launch counts: hipBLASLt (through torch) against
+    this library, both with 16-bit output.  16-bit inputs: torch.matmul on
+    row-major A[M,K] @ B[K,N] (A K-contiguous, B N-contiguous).  E4M3 inputs:
+    torch._scaled_mm with unit scales, which takes B K-contiguous, so both
+    sides read the workload's B bytes as a K-contiguous B (layout NT) and
+    write bf16.  A reference point only; nothing in the library calls torch."""
     import torch
-    if w["dtype"] == synth.E4M3 or tuple(layout) != ("K", "MN") or p.lda != K or p.ldb != N:
+    if tuple(layout) != ("K", "MN") or p.lda != K or p.ldb != N:
         return None
-    tdt = torch.bfloat16 if w["dtype"] == synth.BF16 else torch.float16
-    gd = DTYPE_CODE[(w["dtype"], "bf16" if w["dtype"] == synth.BF16 else "f16")]
-    At, Bt = A.view(tdt).view(M, K), B.view(tdt).view(K, N)
-    Ct = torch.empty(M, N, dtype=tdt, device="cuda")
+    fp8 = w["dtype"] == synth.E4M3
+    if fp8:
+        if N != K:
+            return None                    # B's bytes reread as K-contiguous B need N == K
+        At = A.view(torch.float8_e4m3fn).view(M, K)
+        Bt = B.view(torch.float8_e4m3fn).view(N, K)
+        one = torch.ones((), device="cuda")
+        Ct = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        gd = DTYPE_CODE[(synth.E4M3, "bf16")]
 
-    def ours():
-        lib.gemm_run(h, A, B, Ct, M, N, K, p.lda, p.ldb, N, 0, 1, gd, stream)
+        def ours():
+            lib.gemm_run(h, A, B, Ct, M, N, K, K, K, N, 0, 0, gd, stream)
 
-    def theirs():
-        torch.matmul(At, Bt, out=Ct)
+        def theirs():
+            torch._scaled_mm(At, Bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    else:
+        tdt = torch.bfloat16 if w["dtype"] == synth.BF16 else torch.float16
+        gd = DTYPE_CODE[(w["dtype"], "bf16" if w["dtype"] == synth.BF16 else "f16")]
+        At, Bt = A.view(tdt).view(M, K), B.view(tdt).view(K, N)
+        Ct = torch.empty(M, N, dtype=tdt, device="cuda")
+
+        def ours():
+            lib.gemm_run(h, A, B, Ct, M, N, K, p.lda, p.ldb, N, 0, 1, gd, stream)
+
+        def theirs():
+            torch.matmul(At, Bt, out=Ct)
 
     def timed(fn):
         for _ in range(warmup):
@@ -160,10 +178,14 @@ def vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p, steps, warmup, stream):
 
     res = {}
     for name, fn in (("hipblaslt", theirs), ("library", ours), ("hipblaslt_again", theirs)):
+        t0 = time.time()
         ms = timed(fn)
+        log(f"vs-hipblaslt {name}: {ms:.5f} ms, wall clock {t0:.1f} .. {time.time():.1f}")
         res[name + "_ms"] = round(ms, 5)
         res[name + "_tflops"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
-    res["output"] = "bf16" if w["dtype"] == synth.BF16 else "f16"
+    res["output"] = "f16" if w["dtype"] == synth.F16 else "bf16"
+    if fp8:
+        res["layout"] = "NT"
     return res
 
 

@@ -37,3 +37,22 @@ def test_bench_prints_one_complete_json_line():
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert cpu["unit"] == "TFLOP/s" and cpu["sample"]
+
+
+@pytest.mark.parametrize("workload,output", [("f16_1500x1152x896_nn_f16", "f16"),
+                                             ("e4m3_8192_nn_f32", "bf16")])
+def test_bench_vs_hipblaslt_reports_both_sides(workload, output):
+    """The hipBLASLt reference point: both sides timed on the same operands."""
+    print(f"CASE bench.py --workload {workload} --vs-hipblaslt --steps 3 --warmup 3", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
+                        "--steps", "3", "--warmup", "3", "--no-cpu-baseline", "--no-graph",
+                        "--no-flushed", "--vs-hipblaslt"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    v = d["config"]["vs_hipblaslt"]
+    assert v is not None and v["output"] == output
+    for side in ("hipblaslt", "library", "hipblaslt_again"):
+        assert v[side + "_ms"] > 0 and v[side + "_tflops"] > 0
+    if workload.startswith("e4m3"):
+        assert v["layout"] == "NT"
