@@ -74,7 +74,7 @@ enum gemm_dtype {
 enum gemm_status {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = 1,   /* bad enum, negative size, NULL pointer, ld too small, C overlaps A/B */
-    GEMM_ERR_UNSUPPORTED = 2,   /* valid request the kernels cannot serve: misaligned pointer or ld, size of 2^30 or more */
+    GEMM_ERR_UNSUPPORTED = 2,   /* valid request the kernels cannot serve: misaligned pointer or ld, size of 2^30 or more, an operand spanning 2^63 bytes or more */
     GEMM_ERR_DEVICE = 3,        /* no device, not a gfx950 device, or the current device is not the handle's */
     GEMM_ERR_LAUNCH = 4         /* the HIP runtime rejected the kernel launch */
 };
@@ -92,7 +92,8 @@ int gemm_create(gemm_handle_t *out);
  *              multiples of 16 elements, else GEMM_ERR_UNSUPPORTED.
  *   C          device pointer to fp32 (4-byte aligned) or bf16/fp16
  *              (2-byte aligned) elements; must not overlap A or B.
- *   M, N, K    sizes, 0 <= size < 2^30; lda, ldb, ldc < 2^40.  M == 0 or N == 0 is a no-op;
+ *   M, N, K    sizes, 0 <= size < 2^30; lda, ldb, ldc < 2^40; no operand may span 2^63 bytes
+ *              or more ((rows - 1) * ld + row length, in bytes).  M == 0 or N == 0 is a no-op;
  *              K == 0 writes zeros (the empty sum) to the M x N block of C.
  *   lda        >= K (layoutA K-contig) or >= M (MN-contig)
  *   ldb        >= N (layoutB MN-contig) or >= K (K-contig)

@@ -194,6 +194,17 @@ static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t
   return launch_dtype<Small>(a, la, lb, dtype, s);
 }
 
+// Bytes spanned by `outer` rows of `inner` elements of `es` bytes at leading
+// dimension `ld`, i.e. ((outer - 1) * ld + inner) * es, or -1 when that does
+// not fit in 63 bits (no such buffer can exist).
+static int64_t footprint_bytes(int64_t outer, int64_t ld, int64_t inner, int64_t es) {
+  int64_t r;
+  if (__builtin_mul_overflow(outer - 1, ld, &r) || __builtin_add_overflow(r, inner, &r) ||
+      __builtin_mul_overflow(r, es, &r))
+    return -1;
+  return r;
+}
+
 static bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
   const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
@@ -268,16 +279,13 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, void *C, int64_t M, 
   }
   if ((uintptr_t)C & (uintptr_t)(out_size - 1)) return GEMM_ERR_UNSUPPORTED;
 
-  const int64_t c_bytes = ((M - 1) * ldc + N) * out_size;
-  if (K > 0) {
-    const int64_t a_bytes = ((a_outer - 1) * lda + a_inner) * es;
-    const int64_t b_bytes = ((b_outer - 1) * ldb + b_inner) * es;
-    if (ranges_overlap(C, c_bytes, A, a_bytes) || ranges_overlap(C, c_bytes, B, b_bytes))
-      return GEMM_ERR_INVALID_ARG;
-  }
+  const int64_t c_bytes = footprint_bytes(M, ldc, N, out_size);
+  const int64_t a_fp = K > 0 ? footprint_bytes(a_outer, lda, a_inner, es) : 0;
+  const int64_t b_fp = K > 0 ? footprint_bytes(b_outer, ldb, b_inner, es) : 0;
+  if (c_bytes < 0 || a_fp < 0 || b_fp < 0) return GEMM_ERR_UNSUPPORTED;
+  if (K > 0 && (ranges_overlap(C, c_bytes, A, a_fp) || ranges_overlap(C, c_bytes, B, b_fp)))
+    return GEMM_ERR_INVALID_ARG;
 
-  const int64_t a_fp = K > 0 ? ((a_outer - 1) * lda + a_inner) * es : 0;
-  const int64_t b_fp = K > 0 ? ((b_outer - 1) * ldb + b_inner) * es : 0;
   const Args args{(const uint16_t *)A, (const uint16_t *)B, C, (int)M, (int)N, (int)K,
                   lda, ldb, ldc, (uint32_t)(a_fp < ((int64_t)1 << 31) ? a_fp : 0),
                   (uint32_t)(b_fp < ((int64_t)1 << 31) ? b_fp : 0)};

@@ -114,6 +114,9 @@ A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addr
     ((A0, B0, C0, 16, 16, 12, 12, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # lda % 8
     ((A0, B0, C0, 16, 16, 16, 16, 20, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),  # ldb % 8
     ((A0, B0, C0, 1 << 30, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
+    # footprints beyond 2^63 bytes: (M - 1) * ldc * 4 and (M - 1) * lda * 2 overflow int64
+    ((A0, B0, C0, 1 << 29, 16, 16, 16, 16, (1 << 39) + 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
+    ((A0, B0, C0, 1 << 29, 16, 16, (1 << 40) - 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
     ((A0, B0, A0 + 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C in A
     ((A0, B0, B0 - 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C over B
     ((A0, B0, A0 + 512, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),    # just past A
