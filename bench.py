@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layout", default=None, help="e.g. K,MN (A contiguity, B contiguity)")
+    ap.add_argument("--shape", default=None,
+                    help="M,N,K: the workload's types, layout and values on another shape "
+                         "(a diagnostic line: no traffic or bank-conflict figures)")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of C the oracle computes for the CPU baseline "
                          "(default: about 6e10 flops' worth, 10-20 s on 16 cores)")
@@ -207,7 +210,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
-                         "(noswizzle, scalar_tr, ring2, noxcd, stage1) instead of the library")
+                         "(noswizzle, scalar_tr, ring2, noxcd, stage1, small2) instead of the library")
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
@@ -241,6 +244,11 @@ def main():
         return
 
     w = dict(synth.WORKLOADS[args.workload])
+    if args.shape:
+        dims = [int(x) for x in args.shape.split(",")]
+        if len(dims) != 3 or min(dims) < 1:
+            sys.exit("--shape takes M,N,K, three positive sizes")
+        w["M"], w["N"], w["K"] = dims
     layout = tuple(args.layout.split(",")) if args.layout else w["layouts"][0]
     gd = DTYPE_CODE[(w["dtype"], w["out"])]
     M, N, K = w["M"], w["N"], w["K"]
@@ -345,8 +353,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak_tflops, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4)}
     src_hash = kernel_source_hash()
-    roof["traffic"] = read_traffic(args.workload, src_hash) if layout == tuple(w["layouts"][0]) \
-        else None
+    roof["traffic"] = read_traffic(args.workload, src_hash) \
+        if layout == tuple(w["layouts"][0]) and not args.shape else None
 
     log(f"kernel ms: mean {kavg:.4f} median {np.median(kern_ms):.4f} min {kern_ms.min():.4f}; "
         f"flushed-cache median {np.median(fl_ms) if fl_ms else float('nan'):.4f} ms; "
@@ -385,8 +393,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    line["config"]["lds_bank_conflict_rate"] = None if args.variant else \
+    line["config"]["lds_bank_conflict_rate"] = None if args.variant or args.shape else \
         read_conflict_rate(args.workload, line["config"]["layout"], src_hash)
+    if args.shape:
+        line["config"]["name"] = f"{args.workload} at {M}x{N}x{K}"
     if args.variant:
         line["config"]["ablation_build"] = args.variant
         roof["traffic"] = None

@@ -29,6 +29,7 @@ VARIANTS = {
     "ring2": ["-DLSM_RING_STAGES=2"],       # M <= 32 kernel with a 2-stage instead of 6-stage ring
     "noxcd": ["-DLSM_XCD_REMAP=0"],         # tiles in hardware workgroup order, not grouped per XCD
     "stage1": ["-DLSM_DMA_STAGES=1"],       # 128/64 direct-to-LDS kernel with one LDS stage, no overlap
+    "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

@@ -64,7 +64,8 @@ struct Args {
   uint32_t a_bytes, b_bytes;   // operand footprints (used by the direct-to-LDS kernel)
 };
 
-enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3 };
+// DMA4: the direct-to-LDS kernel with four LDS stages (operand panels beyond the L2).
+enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3, DMA4 = 4 };
 
 template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_dma(const Args &a, hipStream_t stream) {
@@ -82,6 +83,8 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   const void *fn;
   if constexpr (KIND == PINGPONG)
     fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT>;
+  else if constexpr (KIND == DMA4)
+    fn = (const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT, 4>;
   else
     fn = (const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT>;
   return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(T::NT), params, 0, stream);
@@ -164,10 +167,33 @@ static bool dma_ok(const Args &a, int la, int lb, int64_t es) {
          (b_outer + 512) * a.ldb * es + es * (int64_t)a.K < lim;
 }
 
+// One XCD's L2 on MI355X.
+constexpr int64_t kL2BytesPerXcd = (int64_t)4 << 20;
+
+// The 64 x 64 tile takes four LDS stages when the operand panels that one
+// XCD's workgroups read over the whole K range do not fit in its L2: its K
+// steps are short (four MFMAs per wave and K tile, two for 8-bit inputs), so
+// with the loads only one tile ahead it waits on the longer latency of loads
+// the L2 misses.  Measured on MI355X (kernel traces): 512 x 512 x 4096 and
+// 1024 x 1024 x 4096 take 22 us with four stages against 31 us with two;
+// while the panels fit, four stages are 11-16% slower.
+// LSM_SMALL_FOUR_STAGES = 0 (an A/B build only) keeps the double buffer for
+// every shape; the library is built with 1.
+#ifndef LSM_SMALL_FOUR_STAGES
+#define LSM_SMALL_FOUR_STAGES 1
+#endif
+static bool small_tile_four_stages(const Args &a, int64_t es) {
+  if (!LSM_SMALL_FOUR_STAGES) return false;
+  const long long panel = 64LL * a.K * es;
+  return xcd_max_panel_bytes((int)ceil_div(a.M, 64), (int)ceil_div(a.N, 64), 8, panel, panel) >
+         kL2BytesPerXcd;
+}
+
 // Shape classes.  M <= 32 takes the split-K ring kernel (HBM-bound).
 // Otherwise the big tile when it still gives every CU at least one
 // workgroup, else the 128 tile when that does, else the 64 tile (a short,
-// latency-bound K loop per workgroup; more workgroups hide more of it).
+// latency-bound K loop per workgroup; more workgroups hide more of it),
+// with four LDS stages when its operand panels overflow the L2.
 // Shapes whose contiguous extents are not whole 16-byte chunks (dma_ok()
 // false) take the register-staged kernel of the same class.
 // 8-bit inputs run on the direct-to-LDS kernels only (gemm_run rejects fp8
@@ -179,6 +205,7 @@ static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t
     if (a.M <= 32) return launch_fp8<SkinnyStream8, SKINNY>(a, la, lb, dtype, s);
     if (t256 >= 256) return launch_fp8<PingPong8, PINGPONG>(a, la, lb, dtype, s);
     if (t128 >= 256) return launch_fp8<DmaMid8, DMA>(a, la, lb, dtype, s);
+    if (small_tile_four_stages(a, 1)) return launch_fp8<DmaSmall8, DMA4>(a, la, lb, dtype, s);
     return launch_fp8<DmaSmall8, DMA>(a, la, lb, dtype, s);
   }
   const bool dma = dma_ok(a, la, lb, 2);
@@ -186,6 +213,7 @@ static hipError_t dispatch(const Args &a, int la, int lb, int dtype, hipStream_t
     if (a.M <= 32) return launch_dtype<SkinnyStream, SKINNY>(a, la, lb, dtype, s);
     if (t256 >= 256) return launch_dtype<PingPong, PINGPONG>(a, la, lb, dtype, s);
     if (t128 >= 256) return launch_dtype<DmaMid, DMA>(a, la, lb, dtype, s);
+    if (small_tile_four_stages(a, 2)) return launch_dtype<DmaSmall, DMA4>(a, la, lb, dtype, s);
     return launch_dtype<DmaSmall, DMA>(a, la, lb, dtype, s);
   }
   if (a.M <= 32) return launch_dtype<Skinny>(a, la, lb, dtype, s);

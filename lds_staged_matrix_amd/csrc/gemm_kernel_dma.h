@@ -169,7 +169,21 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
 #define LSM_DMA_STAGES 2
 #endif
 
-template <class T, int LA, int LB, int IN, int OUT>
+// Wait until at most `n` (0..3) K tiles' loads, LPT per thread each, are
+// still in flight (loads complete in issue order).
+template <int LPT>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPT) : "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPT) : "memory");
+}
+
+// NS = number of LDS stages: 2 (double buffer), or 4 for a K loop whose
+// operand panels overflow the L2 and come from further out: then the loads
+// of tile kt+4 go out as soon as tile kt's stage is free, three tiles ahead
+// of their use instead of one.
+template <class T, int LA, int LB, int IN, int OUT, int NS = 2>
 __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
@@ -181,8 +195,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   using F = Frags<T, IN>;
   static_assert(KSTEPS % 2 == 0, "the register double buffer alternates two k-steps");
   constexpr int STAGE = OA::BYTES + OB::BYTES;
-  constexpr int STAGES = LSM_DMA_STAGES;
-  static_assert(STAGES == 1 || STAGES == 2, "one or two LDS stages");
+  constexpr int STAGES = LSM_DMA_STAGES == 1 ? 1 : NS;
+  static_assert(STAGES == 1 || STAGES == 2 || STAGES == 4, "one, two or four LDS stages");
+  constexpr int LPT = OA::LOADS + OB::LOADS;              // loads per thread and K tile
+  static_assert(3 * LPT <= 63, "vmcnt counts up to 63");
   constexpr int READS = T::FM * frag_reads<OA, IN>() + T::FN * frag_reads<OB, IN>();
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
 
   auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (uint32_t)((STAGES == 1 ? 0 : kt & 1) * STAGE);
+    const uint32_t st = lds0 + (uint32_t)((kt & (STAGES - 1)) * STAGE);
     const int k0 = kt * T::BK;
     uint32_t av = a_voff, bv = b_voff;
     if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
@@ -250,15 +266,22 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
     }
   } else {
   if (KT > 0) {
-    issue(0);
-    wait_dma();
-    __syncthreads();                       // tile 0 is in stage 0
-    if (KT > 1) issue(1);                  // tile 1 -> stage 1, lands during step 0
+    if constexpr (STAGES == 2) {
+      issue(0);
+      wait_dma();
+      __syncthreads();                     // tile 0 is in stage 0
+      if (KT > 1) issue(1);                // tile 1 -> stage 1, lands during step 0
+    } else {
+      const int pro = KT < STAGES ? KT : STAGES;   // tiles 0 .. pro-1, one per stage
+      for (int t = 0; t < pro; ++t) issue(t);
+      wait_tiles<LPT>(pro - 1);            // tile 0 landed, the others may be in flight
+      __syncthreads();                     // tile 0 is in stage 0
+    }
     read_frags<T, IN, OA, OB>(cur, smem, smem + OA::BYTES, lane, wm, wn, 0);
   }
 
   for (int kt = 0; kt < KT; ++kt) {
-    const char *sA = smem + (kt & 1) * STAGE;
+    const char *sA = smem + (kt & (STAGES - 1)) * STAGE;
     const char *sB = sA + OA::BYTES;
 #pragma unroll
     for (int kk = 0; kk + 1 < KSTEPS; kk += 2) {
@@ -281,11 +304,17 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
         for (int j = 0; j < T::FN; j++) pin_acc(acc[i][j]);
     }
     if (kt + 1 < KT) {
-      wait_dma();
-      __syncthreads();                     // tile kt+1 is in stage (kt+1)&1; stage kt&1 is free
-      const char *nA = smem + ((kt + 1) & 1) * STAGE;
+      if constexpr (STAGES == 2) {
+        wait_dma();
+      } else {
+        // tile kt+1 landed; tiles kt+2 .. kt+STAGES-1 may still be in flight
+        const int ahead = KT - kt - 2 < STAGES - 2 ? KT - kt - 2 : STAGES - 2;
+        wait_tiles<LPT>(ahead);
+      }
+      __syncthreads();                     // tile kt+1 is in its stage; stage kt's is free
+      const char *nA = smem + ((kt + 1) & (STAGES - 1)) * STAGE;
       read_frags<T, IN, OA, OB>(cur, nA, nA + OA::BYTES, lane, wm, wn, 0);
-      if (kt + 2 < KT) issue(kt + 2);
+      if (kt + STAGES < KT) issue(kt + STAGES);
     }
     mfma_block<T, IN>(acc, nxt);
   }

@@ -34,4 +34,8 @@ int lsm_xcd_logical_id(int bid, int nwg) { return lsm::xcd_logical_id(bid, nwg);
 void lsm_tile_coords(int lid, int tiles_m, int tiles_n, int group_m, int *tm, int *tn) {
   lsm::tile_coords(lid, tiles_m, tiles_n, group_m, *tm, *tn);
 }
+long long lsm_xcd_max_panel_bytes(int tiles_m, int tiles_n, int group_m, long long a_panel,
+                                  long long b_panel) {
+  return lsm::xcd_max_panel_bytes(tiles_m, tiles_n, group_m, a_panel, b_panel);
+}
 }

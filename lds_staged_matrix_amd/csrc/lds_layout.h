@@ -176,4 +176,52 @@ __host__ __device__ inline void tile_coords(int lid, int tiles_m, int tiles_n, i
   tn = in / gm;
 }
 
+// Operand bytes one XCD's workgroups touch over the whole K range, largest
+// over the 8 XCDs: the distinct tile rows (A panels of `a_panel` bytes) plus
+// the distinct tile columns (B panels of `b_panel` bytes) of that XCD's
+// contiguous range of logical ids under tile_coords.  When this exceeds one
+// XCD's L2, the panels cannot stay resident while the XCD's workgroups
+// stream through K, and the loads come from further out.
+__host__ __device__ inline long long xcd_max_panel_bytes(int tiles_m, int tiles_n, int group_m,
+                                                         long long a_panel, long long b_panel) {
+  const int nwg = tiles_m * tiles_n;
+  const int width = group_m * tiles_n;              // logical ids per group of tile rows
+  long long most = 0;
+  for (int x = 0; x < 8; x++) {
+    const int cnt = (nwg >> 3) + (x < (nwg & 7) ? 1 : 0);
+    if (cnt == 0) continue;
+    const int lo = x * (nwg >> 3) + (x < (nwg & 7) ? x : (nwg & 7));
+    const int hi = lo + cnt;                         // this XCD's ids: [lo, hi)
+    const int g0 = lo / width, g1 = (hi - 1) / width;
+    int rows = 0, first_c0 = 0, last_c1 = 0;
+    for (int g = g0; g <= g1; g++) {
+      const int first_m = g * group_m;
+      const int gm = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+      const int a = (lo > g * width ? lo : g * width) - g * width;     // [a, b) inside the group
+      const int b = (hi < g * width + gm * tiles_n ? hi : g * width + gm * tiles_n) - g * width;
+      const int c0 = a / gm, c1 = (b - 1) / gm;      // columns touched in this group
+      if (c1 == c0)
+        rows += b - a;
+      else if (c1 == c0 + 1)                         // two partial columns
+        rows += (gm - a % gm) + ((b - 1) % gm + 1) < gm ? (gm - a % gm) + ((b - 1) % gm + 1) : gm;
+      else
+        rows += gm;
+      if (g == g0) first_c0 = c0;
+      if (g == g1) last_c1 = c1;
+    }
+    // Columns: one group -> [first_c0, last_c1]; two -> the first group's tail
+    // [first_c0, tiles_n) and the last group's head [0, last_c1]; more -> all.
+    int cols;
+    if (g1 == g0)
+      cols = last_c1 - first_c0 + 1;
+    else if (g1 == g0 + 1)
+      cols = last_c1 + 1 >= first_c0 ? tiles_n : (last_c1 + 1) + (tiles_n - first_c0);
+    else
+      cols = tiles_n;
+    const long long bytes = rows * a_panel + cols * b_panel;
+    if (bytes > most) most = bytes;
+  }
+  return most;
+}
+
 }  // namespace lsm

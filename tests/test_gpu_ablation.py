@@ -1,7 +1,8 @@
 """The A/B builds (one design choice changed each: no LDS swizzle, scalar
 16-bit reads instead of ds_read_b64_tr_b16, a 2-stage ring for M <= 32,
 tiles in hardware workgroup order instead of the per-XCD order, one LDS
-stage instead of two in the direct-to-LDS kernel)
+stage instead of two in the direct-to-LDS kernel, the 64 x 64 tile without
+its four-stage pipeline)
 compute the same products: bit-identical to the library on integer-valued
 inputs, whose result is unique.  Their speed and counters are what the
 benchmark compares; this checks that they are the same computation."""
@@ -15,10 +16,12 @@ import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1"]
+VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1", "small2"]
 # one shape per kernel: ping-pong (>= 256 tiles of 256), 128 x 128 tile
-# (>= 256 tiles of 128), 64 x 64 tile, split-K ring (M <= 32)
-SHAPES = [(4096, 4096, 136), (2048, 2056, 200), (520, 264, 1000), (32, 1000, 1032)]
+# (>= 256 tiles of 128), 64 x 64 tile with two and with four LDS stages (its
+# operand panels beyond one XCD's L2), split-K ring (M <= 32)
+SHAPES = [(4096, 4096, 136), (2048, 2056, 200), (520, 264, 1000), (500, 300, 6152),
+          (32, 1000, 1032)]
 LAYOUTS = [("K", "MN"), ("K", "K"), ("MN", "MN"), ("MN", "K")]
 
 
