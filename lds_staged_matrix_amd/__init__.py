@@ -76,6 +76,22 @@ def _ptr(x):
     return int(x)
 
 
+def _int(x, bits, name):
+    """x as a Python int that fits the C ABI's signed `bits`-bit parameter.
+    ctypes would silently keep only the low bits of a larger value."""
+    v = int(x)
+    if not -(1 << (bits - 1)) <= v < (1 << (bits - 1)):
+        raise OverflowError(f"{name}={v} does not fit the C ABI's int{bits}_t parameter")
+    return v
+
+
+def _sizes(M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype):
+    return ([_int(v, 64, n) for v, n in zip((M, N, K, lda, ldb, ldc),
+                                             ("M", "N", "K", "lda", "ldb", "ldc"))] +
+            [_int(v, 32, n) for v, n in zip((layoutA, layoutB, dtype),
+                                             ("layoutA", "layoutB", "dtype"))])
+
+
 def _stream(s):
     if s is None:
         return None
@@ -95,8 +111,9 @@ def gemm_create():
 
 def gemm_run(h, A, B, C, M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype, stream=None) -> int:
     """Enqueue C <- A*B; returns the gemm_status code (0 on success)."""
-    return load_library().gemm_run(h, _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
-                                   layoutA, layoutB, dtype, _stream(stream))
+    return load_library().gemm_run(h, _ptr(A), _ptr(B), _ptr(C),
+                                   *_sizes(M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype),
+                                   _stream(stream))
 
 
 def gemm_destroy(h) -> int:
@@ -104,7 +121,7 @@ def gemm_destroy(h) -> int:
 
 
 def gemm_status_str(status: int) -> str:
-    return load_library().gemm_status_str(status).decode()
+    return load_library().gemm_status_str(_int(status, 32, "status")).decode()
 
 
 class Library:
@@ -124,14 +141,15 @@ class Library:
 
     def gemm_run(self, h, A, B, C, M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype,
                  stream=None) -> int:
-        return self._lib.gemm_run(h, _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
-                                  layoutA, layoutB, dtype, _stream(stream))
+        return self._lib.gemm_run(h, _ptr(A), _ptr(B), _ptr(C),
+                                  *_sizes(M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype),
+                                  _stream(stream))
 
     def gemm_destroy(self, h) -> int:
         return self._lib.gemm_destroy(h)
 
     def gemm_status_str(self, status: int) -> str:
-        return self._lib.gemm_status_str(status).decode()
+        return self._lib.gemm_status_str(_int(status, 32, "status")).decode()
 
 
 def ablation_library(name: str) -> Library:

@@ -158,13 +158,18 @@ static bool is_fp8(int dtype) { return dtype == GEMM_E4M3_F32 || dtype == GEMM_E
 // The direct-to-LDS kernels need whole 16-byte chunks along each operand's
 // contiguous dimension, and byte offsets (footprint plus one tile of rows of
 // overhang, plus a K advance) below 2^31 for their 32-bit buffer offsets.
+static bool offsets_fit_31_bits(int64_t outer, int64_t ld, int64_t es, int64_t K) {
+  int64_t r;
+  return !__builtin_mul_overflow(outer + 512, ld, &r) && !__builtin_mul_overflow(r, es, &r) &&
+         !__builtin_add_overflow(r, es * K, &r) && r < ((int64_t)1 << 31);
+}
+
 static bool dma_ok(const Args &a, int la, int lb, int64_t es) {
   const int64_t a_inner = la == KC ? a.K : a.M, a_outer = la == KC ? a.M : a.K;
   const int64_t b_inner = lb == MNC ? a.N : a.K, b_outer = lb == MNC ? a.K : a.N;
-  const int64_t lim = (int64_t)1 << 31;
   return (a_inner * es) % 16 == 0 && (b_inner * es) % 16 == 0 &&
-         (a_outer + 512) * a.lda * es + es * (int64_t)a.K < lim &&
-         (b_outer + 512) * a.ldb * es + es * (int64_t)a.K < lim;
+         offsets_fit_31_bits(a_outer, a.lda, es, a.K) &&
+         offsets_fit_31_bits(b_outer, a.ldb, es, a.K);
 }
 
 // One XCD's L2 on MI355X.

@@ -117,9 +117,26 @@ A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addr
     # footprints beyond 2^63 bytes: (M - 1) * ldc * 4 and (M - 1) * lda * 2 overflow int64
     ((A0, B0, C0, 1 << 29, 16, 16, 16, 16, (1 << 39) + 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
     ((A0, B0, C0, 1 << 29, 16, 16, (1 << 40) - 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_UNSUPPORTED),
+    # E4M3: A's footprint (M - 1) * lda is below 2^63 bytes, but the 32-bit offset check's
+    # (M + 512) * lda is not; the shape must be refused, not reach the device
+    ((1 << 40, B0, C0, 1 << 23, 16, 16, (1 << 40) - 16, 16, 16, 0, 1, 4),
+     lsm.GEMM_ERR_UNSUPPORTED),
     ((A0, B0, A0 + 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C in A
     ((A0, B0, B0 - 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C over B
     ((A0, B0, A0 + 512, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),    # just past A
 ])
 def test_validation(lib, args, status):
     assert lsm.gemm_run(FAKE, *args) == status
+
+
+@pytest.mark.parametrize("pos,value", [(3, 1 << 64), (5, -(1 << 63) - 1), (8, 1 << 63),
+                                       (9, (1 << 32) + 1), (10, 1 << 31), (11, -(1 << 31) - 1)])
+def test_binding_refuses_integers_the_abi_cannot_hold(lib, pos, value):
+    """ctypes would pass only the low bits (2^64 + 16 as 16, 2^32 + 1 as 1):
+    the binding raises instead of handing the library a different request."""
+    args = [A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0]
+    args[pos] = value
+    with pytest.raises(OverflowError):
+        lsm.gemm_run(FAKE, *args)
+    with pytest.raises(OverflowError):
+        lsm.gemm_status_str(1 << 32)
