@@ -67,6 +67,13 @@ struct Args {
 // DMA4: the direct-to-LDS kernel with four LDS stages (operand panels beyond the L2).
 enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3, DMA4 = 4 };
 
+// LSM_PP_MFMA = 16 builds the ping-pong kernel's 16-bit instances with
+// v_mfma_f32_16x16x32 instead of v_mfma_f32_32x32x16; it exists only for the
+// A/B build that measures the MFMA shape.  The library is built with 32.
+#ifndef LSM_PP_MFMA
+#define LSM_PP_MFMA 32
+#endif
+
 template <class T, int KIND, int LA, int LB, int IN, int OUT>
 static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   int tiles_m = (a.M + T::BM - 1) / T::BM;
@@ -82,7 +89,8 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   void *params[] = {&A, &B, &C, &M, &N, &K, &lda, &ldb, &ldc, &tiles_m, &tiles_n, &ab, &bb, &c_vec};
   const void *fn;
   if constexpr (KIND == PINGPONG)
-    fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT>;
+    fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT,
+                                                IN == IN_E4M3 ? 32 : LSM_PP_MFMA>;
   else if constexpr (KIND == DMA4)
     fn = (const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT, 4>;
   else

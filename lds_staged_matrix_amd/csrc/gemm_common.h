@@ -22,6 +22,7 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef _Float16 v8f16 __attribute__((ext_vector_type(8)));
 typedef float v16f32 __attribute__((ext_vector_type(16)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef int v8i32 __attribute__((ext_vector_type(8)));
@@ -107,9 +108,50 @@ __device__ __forceinline__ v16f32 mfma_step(typename InT<IN>::frag a, typename I
     return mfma_32x32x16<IN>(a, b, c);
 }
 
+// One 16 x 16 MFMA step (k = 32) on 16-bit inputs: the 16 x 16 A/B build of
+// the ping-pong kernel ("Lds Optimization", "Optimization Method 3: Increase
+// Write-Read Distance", names v_mfma_f32_16x16x32 as the MFMA it overlaps).
+template <int IN>
+__device__ __forceinline__ v4f32 mfma_16x16x32(v8i16 a, v8i16 b, v4f32 c) {
+  static_assert(IN != IN_E4M3, "16-bit inputs only");
+  if constexpr (IN == IN_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, a),
+                                                   __builtin_bit_cast(v8bf16, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8f16, a),
+                                                  __builtin_bit_cast(v8f16, b), c, 0, 0, 0);
+}
+
+// Accumulator layouts of the two MFMA shapes.  Register r of lane l holds
+//   32 x 32 block (16 registers): row 8*(r >> 2) + 4*(l >> 5) + (r & 3), column l & 31
+//     (checked with a probe);
+//   16 x 16 block (4 registers):  row 4*(l >> 4) + r, column l & 15.
+// row() is the whole row; lane_row() + reg_row() splits it into its lane and register parts.
+template <int MF>
+struct AccLayout;
+template <>
+struct AccLayout<32> {
+  static constexpr int F = 32, R = 16;
+  typedef v16f32 type;
+  __device__ static constexpr int lane_row(int lane) { return 4 * (lane >> 5); }
+  __device__ static constexpr int reg_row(int r) { return 8 * (r >> 2) + (r & 3); }
+  __device__ static constexpr int row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+  __device__ static constexpr int col(int lane) { return lane & 31; }
+};
+template <>
+struct AccLayout<16> {
+  static constexpr int F = 16, R = 4;
+  typedef v4f32 type;
+  __device__ static constexpr int lane_row(int lane) { return 4 * (lane >> 4); }
+  __device__ static constexpr int reg_row(int r) { return r; }
+  __device__ static constexpr int row(int r, int lane) { return 4 * (lane >> 4) + r; }
+  __device__ static constexpr int col(int lane) { return lane & 15; }
+};
+
 // Keeps an accumulator's MFMAs ahead of this point: the compiler may otherwise
 // sink register-only MFMAs past a following barrier into the next phase.
 __device__ __forceinline__ void pin_acc(v16f32 &c) { asm volatile("" : "+v"(c)); }
+__device__ __forceinline__ void pin_acc(v4f32 &c) { asm volatile("" : "+v"(c)); }
 
 // One 32x32x16 operand fragment: lane l gets row/column (l & 31) of the
 // fragment starting at `base`, k = 16*kk + 8*(l >> 5) + 0..7.
@@ -154,6 +196,30 @@ __device__ __forceinline__ v8i16 read_frag(const char *lds, int lane, int base, 
   }
 }
 
+// One 16 x 32 operand fragment of v_mfma_f32_16x16x32 (k-step kk of 32):
+// lane l gets row/column (l & 15) of the fragment starting at `base`,
+// k = 32*kk + 8*(l >> 4) + 0..7.
+template <class OT>
+__device__ __forceinline__ v8i16 read_frag16(const char *lds, int lane, int base, int kk) {
+  if constexpr (OT::kcontig) {
+    return *(const v8i16 *)(lds + frag16_kc_offset(lane, base, kk, OT::ROW_BYTES));
+  } else if constexpr (!LSM_TR_READ) {
+    const int col = base + (lane & 15);
+    v8i16 f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      f[i] = *(const short *)(lds + mn_chunk_offset(32 * kk + 8 * (lane >> 4) + i, col / 8,
+                                                    OT::ROW_BYTES) + 2 * (col & 7));
+    return f;
+  } else {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(lds + frag16_tr_offset(lane, base, kk, 0, OT::ROW_BYTES)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(lds + frag16_tr_offset(lane, base, kk, 1, OT::ROW_BYTES)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
 // C is written with non-temporal stores: nothing in the kernel reads it back,
 // and on MI355X streaming it past the caches gave the fp32 8192^3 case 3-5%.
 template <int OUT>
@@ -178,34 +244,36 @@ struct OutElem<OUT_BF16> { typedef __bf16 type; };
 template <>
 struct OutElem<OUT_F16> { typedef _Float16 type; };
 
-// Epilogue: accumulator register r of lane l holds row
-// 8*(r >> 2) + 4*(l >> 5) + (r & 3) and column (l & 31) of its 32x32 block
-// (layout checked with a probe).  Interior tiles store unmasked; edge tiles
-// mask rows >= M and columns >= N.
-template <class T, int OUT>
-__device__ __forceinline__ void epilogue(void *C, const v16f32 (&acc)[T::FM][T::FN], int M, int N,
-                                         int64_t ldc, int m0, int n0, int wm, int wn, int lane) {
+// Epilogue: each wave stores its accumulator blocks (layout AccLayout<MF>)
+// straight from registers.  Interior tiles store unmasked; edge tiles mask
+// rows >= M and columns >= N.
+template <class T, int OUT, int MF = 32>
+__device__ __forceinline__ void epilogue(void *C,
+                                         const typename AccLayout<MF>::type (&acc)[T::TM / MF][T::TN / MF],
+                                         int M, int N, int64_t ldc, int m0, int n0, int wm, int wn,
+                                         int lane) {
+  using L = AccLayout<MF>;
   const bool interior = M - m0 >= T::BM && N - n0 >= T::BN;
-  const int row0 = m0 + wm * T::TM + 4 * (lane >> 5);
-  const int col0 = n0 + wn * T::TN + (lane & 31);
+  const int row0 = m0 + wm * T::TM + L::lane_row(lane);
+  const int col0 = n0 + wn * T::TN + L::col(lane);
   if (interior) {
 #pragma unroll
-    for (int i = 0; i < T::FM; i++)
+    for (int i = 0; i < T::TM / MF; i++)
 #pragma unroll
-      for (int j = 0; j < T::FN; j++)
+      for (int j = 0; j < T::TN / MF; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r++)
-          store_out<OUT>(C, (int64_t)(row0 + 32 * i + 8 * (r >> 2) + (r & 3)) * ldc + col0 + 32 * j,
+        for (int r = 0; r < L::R; r++)
+          store_out<OUT>(C, (int64_t)(row0 + MF * i + L::reg_row(r)) * ldc + col0 + MF * j,
                          acc[i][j][r]);
   } else {
 #pragma unroll
-    for (int i = 0; i < T::FM; i++)
+    for (int i = 0; i < T::TM / MF; i++)
 #pragma unroll
-      for (int j = 0; j < T::FN; j++)
+      for (int j = 0; j < T::TN / MF; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-          const int col = col0 + 32 * j;
+        for (int r = 0; r < L::R; r++) {
+          const int row = row0 + MF * i + L::reg_row(r);
+          const int col = col0 + MF * j;
           if (row < M && col < N) store_out<OUT>(C, (int64_t)row * ldc + col, acc[i][j][r]);
         }
   }
@@ -221,15 +289,15 @@ __device__ __forceinline__ void epilogue(void *C, const v16f32 (&acc)[T::FM][T::
 // (every wave past its last LDS read of the main loop).  `lds_bytes` is the
 // LDS the kernel owns; the wave tile is staged in passes of as many rows as
 // fit.
-// Region layout: row-major, 64 elements per row; the 16-byte chunk index is
-// XORed with ((row >> 2) & 1) * (chunks per row / 2), so the two 32-lane
-// halves of an accumulator write (rows r and r + 4, same columns) land in
-// different halves of the bank line.  The 16-lane phases of the reads cover
-// one row each: conflict-free.
-template <class T, int OUT, int LDS_BYTES>
-__device__ __forceinline__ void epilogue_lds(void *C, const v16f32 (&acc)[T::FM][T::FN], char *lds,
-                                             int M, int N, int64_t ldc, int m0, int n0, int wm,
-                                             int wn, int wave, int lane) {
+// Region layout: row-major, 64 elements per row, 16-byte chunks swizzled per
+// accumulator layout (epi_stage_offset in lds_layout.h) so that every
+// accumulator write and every 16-byte read is conflict-free.
+template <class T, int OUT, int LDS_BYTES, int MF = 32>
+__device__ __forceinline__ void epilogue_lds(void *C,
+                                             const typename AccLayout<MF>::type (&acc)[T::TM / MF][T::TN / MF],
+                                             char *lds, int M, int N, int64_t ldc, int m0, int n0,
+                                             int wm, int wn, int wave, int lane) {
+  using L = AccLayout<MF>;
   static_assert(T::TN == 64, "wave tile 64 columns wide");
   typedef typename OutElem<OUT>::type E;
   constexpr int ESZ = sizeof(E);
@@ -241,22 +309,20 @@ __device__ __forceinline__ void epilogue_lds(void *C, const v16f32 (&acc)[T::FM]
   static_assert(PR % 32 == 0 && T::TM % PR == 0 && WAVES * PR * ROWB <= LDS_BYTES, "staging fits");
   constexpr int RPI = 64 * 16 / ROWB;                        // rows per 64-lane read
   char *mine = lds + wave * PR * ROWB;
-  auto off = [&](int row, int chunk) {
-    return row * ROWB + 16 * (chunk ^ (((row >> 2) & 1) * (CPR / 2)));
-  };
+  auto off = [&](int row, int chunk) { return epi_stage_offset(row, chunk, ROWB, MF); };
   const int grow0 = m0 + wm * T::TM;
   const int gcol0 = n0 + wn * T::TN;
 #pragma unroll
   for (int pass = 0; pass < T::TM / PR; pass++) {
-    // accumulator blocks i of this pass: rows 32*i .. 32*i + 31 of the wave tile
+    // accumulator blocks i of this pass: rows MF*i .. MF*i + MF - 1 of the wave tile
 #pragma unroll
-    for (int i = pass * PR / 32; i < (pass + 1) * PR / 32; i++)
+    for (int i = pass * PR / MF; i < (pass + 1) * PR / MF; i++)
 #pragma unroll
-      for (int j = 0; j < T::FN; j++)
+      for (int j = 0; j < T::TN / MF; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int row = 32 * i - pass * PR + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = 32 * j + (lane & 31);
+        for (int r = 0; r < L::R; r++) {
+          const int row = MF * i - pass * PR + L::row(r, lane);
+          const int col = MF * j + L::col(lane);
           *(E *)(mine + off(row, col * ESZ / 16) + (col * ESZ) % 16) = (E)acc[i][j][r];
         }
     // The reads below return rows written by other lanes of this wave: LDS

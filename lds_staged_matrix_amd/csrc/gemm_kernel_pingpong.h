@@ -35,6 +35,11 @@
 // The LDS layout, the swizzle on the global side of the loads, the edge
 // handling through buffer range checks and the inline-assembly loads are
 // those of gemm_kernel_dma.h.
+//
+// MF selects the MFMA shape: 32 (v_mfma_f32_32x32x16, and the fp8
+// 32x32x64; the library) or 16 (v_mfma_f32_16x16x32 on 16-bit inputs, an A/B
+// build only: each wave's 128 x 64 block as 8 x 4 blocks of 16 x 16, twice the
+// fragment reads per flop, and the same loads, barriers and LDS layout).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,20 +61,23 @@ __device__ __forceinline__ void wg_barrier() {
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Ping-pong tile: 256 x 256 x 64, waves 2 (M) x 4 (N), wave tile 128 x 64.
-template <class T, int LA, int LB, int IN, int OUT>
+template <class T, int LA, int LB, int IN, int OUT, int MF = 32>
 __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
     uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
+  static_assert(MF == 32 || (MF == 16 && IN != IN_E4M3), "16 x 16 MFMAs on 16-bit inputs only");
+  using L = AccLayout<MF>;
   constexpr int LOADERS = T::NT / 2;                     // group 0 issues every load
   constexpr int ES = InT<IN>::ES;
-  constexpr int KSTEPS = T::BK / InT<IN>::KSTEP;          // MFMA k-steps per K tile
+  constexpr int KSTEPS = T::BK / (MF == 32 ? InT<IN>::KSTEP : 32);   // MFMA k-steps per K tile
+  constexpr int FM = T::TM / MF, FN = T::TN / MF;        // MFMA blocks per wave
   using OA = OperandTile<T::BM, T::BK, LA, LOADERS, ES>;
   using OB = OperandTile<T::BN, T::BK, LB, LOADERS, ES>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int LOADS_PER_TILE = OA::LOADS + OB::LOADS;  // per group-0 wave
-  constexpr int FRAGS = KSTEPS * (T::FM + T::FN);         // fragment reads per memory phase
+  constexpr int FRAGS = KSTEPS * (FM + FN);               // fragment reads per memory phase
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -123,13 +131,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     for (int d = 0; d < LOADS_PER_TILE; d++) issue_one(kt, d, av, bv);
   };
 
-  v16f32 acc[T::FM][T::FN];
+  typename L::type acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < T::FM; i++)
+  for (int i = 0; i < FM; i++)
 #pragma unroll
-    for (int j = 0; j < T::FN; j++)
+    for (int j = 0; j < FN; j++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+      for (int r = 0; r < L::R; r++) acc[i][j][r] = 0.f;
 
   const int KT = (K + T::BK - 1) / T::BK;
   if (KT > 0) {
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     wg_barrier();                                        // b = 0
     if (group == 1) wg_barrier();                        // b = 1: group 1 idles through M(0) of group 0
 
-    typename InT<IN>::frag fa[KSTEPS][T::FM], fb[KSTEPS][T::FN];
+    typename InT<IN>::frag fa[KSTEPS][FM], fb[KSTEPS][FN];
     for (int kt = 0; kt < KT; ++kt) {
       // ---- memory phase M(kt)
       // Group 0 also starts the loads of tile kt+1 (their stage was freed at
@@ -155,32 +163,49 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
       // different counter: two loads after each of the first frag reads.
       const char *sA = smem + (kt & 1) * STAGE;
       const char *sB = sA + OA::BYTES;
-      auto m_phase = [&](auto with_loads) {
+      // `with_loads` compiles the load issue in; `load` then decides at run time.
+      auto m_phase = [&](auto with_loads, bool load) {
         constexpr bool LOAD = decltype(with_loads)::value;
         uint32_t av = 0, bv = 0;
         if constexpr (LOAD) voffs(kt + 1, av, bv);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
-          for (int i = 0; i < T::FM + T::FN; i++) {
-            if (i < T::FM)
-              fa[kk][i] = read_frag_in<OA, IN>(sA, lane, wm * T::TM + 32 * i, kk);
-            else
-              fb[kk][i - T::FM] = read_frag_in<OB, IN>(sB, lane, wn * T::TN + 32 * (i - T::FM), kk);
+          for (int i = 0; i < FM + FN; i++) {
+            if constexpr (MF == 32) {
+              if (i < FM)
+                fa[kk][i] = read_frag_in<OA, IN>(sA, lane, wm * T::TM + 32 * i, kk);
+              else
+                fb[kk][i - FM] = read_frag_in<OB, IN>(sB, lane, wn * T::TN + 32 * (i - FM), kk);
+            } else {
+              if (i < FM)
+                fa[kk][i] = read_frag16<OA>(sA, lane, wm * T::TM + 16 * i, kk);
+              else
+                fb[kk][i - FM] = read_frag16<OB>(sB, lane, wn * T::TN + 16 * (i - FM), kk);
+            }
             if constexpr (LOAD) {
               // spread LOADS_PER_TILE loads evenly over the FRAGS fragment reads
-              const int q = kk * (T::FM + T::FN) + i;
+              const int q = kk * (FM + FN) + i;
+              if (load) {
 #pragma unroll
-              for (int d = q * LOADS_PER_TILE / FRAGS; d < (q + 1) * LOADS_PER_TILE / FRAGS; d++)
-                issue_one(kt + 1, d, av, bv);
+                for (int d = q * LOADS_PER_TILE / FRAGS; d < (q + 1) * LOADS_PER_TILE / FRAGS; d++)
+                  issue_one(kt + 1, d, av, bv);
+              }
             }
           }
         }
       };
-      if (group == 0 && kt >= 1 && kt + 1 < KT)
-        m_phase(std::true_type{});
-      else
-        m_phase(std::false_type{});
+      const bool load_next = group == 0 && kt >= 1 && kt + 1 < KT;
+      if constexpr (MF == 32) {
+        if (load_next)
+          m_phase(std::true_type{}, true);
+        else
+          m_phase(std::false_type{}, false);
+      } else {
+        // one copy of the phase, a uniform branch per load: with a second copy
+        // the 16 x 16 build runs out of registers and spills
+        m_phase(std::true_type{}, load_next);
+      }
       wait_lds_reads();
       wg_barrier();                                      // end of M(kt)
 
@@ -189,14 +214,18 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-        for (int i = 0; i < T::FM; i++)
+        for (int i = 0; i < FM; i++)
 #pragma unroll
-          for (int j = 0; j < T::FN; j++)
-            acc[i][j] = mfma_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+          for (int j = 0; j < FN; j++) {
+            if constexpr (MF == 32)
+              acc[i][j] = mfma_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+            else
+              acc[i][j] = mfma_16x16x32<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+          }
 #pragma unroll
-      for (int i = 0; i < T::FM; i++)
+      for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < T::FN; j++) pin_acc(acc[i][j]);
+        for (int j = 0; j < FN; j++) pin_acc(acc[i][j]);
       __builtin_amdgcn_s_setprio(0);
       if (group == 0) {
         wait_dma();                                      // tile kt+1 landed
@@ -210,9 +239,9 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   // The LDS is free once every wave is past its last fragment read.
   if (c_vec) {
     __syncthreads();
-    epilogue_lds<T, OUT, 2 * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+    epilogue_lds<T, OUT, 2 * STAGE, MF>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
   } else {
-    epilogue<T, OUT>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
+    epilogue<T, OUT, MF>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
   }
 }
 

@@ -21,6 +21,15 @@ int lsm_frag_kc_offset(int lane, int base, int kk, int row_bytes) {
 int lsm_frag_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
   return lsm::frag_tr_offset(lane, base, kk, h, row_bytes);
 }
+int lsm_frag16_kc_offset(int lane, int base, int kk, int row_bytes) {
+  return lsm::frag16_kc_offset(lane, base, kk, row_bytes);
+}
+int lsm_frag16_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
+  return lsm::frag16_tr_offset(lane, base, kk, h, row_bytes);
+}
+int lsm_epi_stage_offset(int row, int chunk, int row_bytes, int mf) {
+  return lsm::epi_stage_offset(row, chunk, row_bytes, mf);
+}
 int lsm_loader_lds_offset8(int id, int row_bytes, int k_contig) {
   return lsm::loader_lds_offset(id, row_bytes, k_contig != 0, 1);
 }

@@ -121,6 +121,25 @@ __host__ __device__ constexpr int frag_tr_offset(int lane, int base, int kk, int
          8 * (lane & 1);
 }
 
+// Fragments of v_mfma_f32_16x16x32_{bf16,f16}, used by the 16 x 16 A/B build
+// of the ping-pong kernel (its results, bit-exact on integer inputs in every
+// layout, confirm the layout): lane l holds operand row/column (l & 15) and
+// k = 8*(l >> 4) + i, i = 0..7; `kk` is the 32-deep k step inside the tile.
+
+// K-contiguous operand: one ds_read_b128 per fragment.
+__host__ __device__ constexpr int frag16_kc_offset(int lane, int base, int kk, int row_bytes) {
+  return kc_chunk_offset(base + (lane & 15), 4 * kk + (lane >> 4), row_bytes);
+}
+
+// MN-contiguous operand: two ds_read_b64_tr_b16 per fragment, half h = 0, 1
+// delivering k = 8*(l >> 4) + 4*h + 0..3.  Source lane l reads k-row
+// 32*kk + 8*(l >> 4) + 4*h + ((l >> 2) & 3) at columns base + 4*(l & 3) .. +3.
+__host__ __device__ constexpr int frag16_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
+  return mn_chunk_offset(32 * kk + 8 * (lane >> 4) + 4 * h + ((lane >> 2) & 3),
+                         (base + 4 * (lane & 3)) / 8, row_bytes) +
+         8 * (lane & 1);
+}
+
 // Fragments of v_mfma_scale_f32_32x32x64_f8f6f4 on 8-bit elements (checked
 // with a probe): lane l holds operand row/column (l & 31) and 32 bytes; the
 // k of byte b only has to be the same for A and B, and here it is
@@ -144,6 +163,24 @@ __host__ __device__ constexpr int frag_tr8_offset(int lane, int base, int kk, in
   return mn_chunk_offset(64 * kk + 32 * (lane >> 5) + 8 * q + ((lane & 15) >> 1),
                          (base + 16 * ((lane >> 4) & 1)) / 16, row_bytes, 1) +
          8 * (lane & 1);
+}
+
+// ---------------------------------------------------------------- epilogue staging
+//
+// The LDS-staged epilogue writes each wave's accumulators, converted to the
+// output type, into a private region with `row_bytes` per row, then reads
+// it back 16 bytes per lane.  The 16-byte chunk index is XORed with a
+// function of the row so that the rows one accumulator write covers land in
+// different banks:
+//   32 x 32 blocks (mf = 32): lanes 0-31 and 32-63 write rows r and r + 4,
+//     XOR ((row >> 2) & 1) * (chunks per row / 2), the two halves of a row;
+//   16 x 16 blocks (mf = 16): the four 16-lane groups write rows r, r + 4,
+//     r + 8, r + 12, XOR ((row >> 2) & 3) * (chunks per row / 4), its quarters.
+// The XOR permutes chunks within a row, so reads of whole rows, 16 bytes per
+// lane, touch every bank once.
+__host__ __device__ constexpr int epi_stage_offset(int row, int chunk, int row_bytes, int mf) {
+  return row * row_bytes + 16 * (chunk ^ (mf == 32 ? ((row >> 2) & 1) * (row_bytes / 32)
+                                                   : ((row >> 2) & 3) * (row_bytes / 64)));
 }
 
 // ---------------------------------------------------------------- workgroup -> tile

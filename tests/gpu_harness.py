@@ -61,9 +61,10 @@ def to_device(bits):
     return torch.from_numpy(b).to("cuda")
 
 
-def run_gpu(p, gdtype, ldc=None, extra_rows=0, stream=None):
+def run_gpu(p, gdtype, ldc=None, extra_rows=0, stream=None, lib=None):
     """C = A*B on the GPU.  Returns (C as numpy: float32 values or uint16 bits,
-    shape (M + extra_rows, ldc)), with canary values outside the M x N block."""
+    shape (M + extra_rows, ldc)), with canary values outside the M x N block.
+    `lib` = (Library, handle) runs an A/B build instead of the library."""
     M, N, K = p.M, p.N, p.K
     ldc = N if ldc is None else ldc
     rows = M + extra_rows
@@ -74,8 +75,9 @@ def run_gpu(p, gdtype, ldc=None, extra_rows=0, stream=None):
     else:
         C = torch.full((max(rows * ldc, 1),), int(CANARY_U16), dtype=torch.int16, device="cuda")
     s = torch.cuda.current_stream() if stream is None else stream
-    st = lsm.gemm_run(handle(), A, B, C, M, N, K, p.lda, p.ldb, ldc, LAYOUT[p.layoutA],
-                      LAYOUT[p.layoutB], gdtype, s)
+    run, h = (lsm.gemm_run, handle()) if lib is None else (lib[0].gemm_run, lib[1])
+    st = run(h, A, B, C, M, N, K, p.lda, p.ldb, ldc, LAYOUT[p.layoutA], LAYOUT[p.layoutB],
+             gdtype, s)
     if st != lsm.GEMM_OK:
         raise lsm.GemmError(st, "gemm_run")
     torch.cuda.synchronize()

@@ -1,0 +1,82 @@
+"""The A/B build of the ping-pong kernel on v_mfma_f32_16x16x32 (build
+variant "mfma16"), against the library and the oracle.
+
+The build changes only the MFMA shape of the 16-bit ping-pong kernel: its
+fragment reads, accumulator layout and both epilogues (the LDS-staged one,
+taken when C rows are 16-byte aligned, and the direct one).  On integer inputs
+the result is unique, so it must equal the library's bit for bit; the
+library's own output is checked against the oracle on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lds_staged_matrix_amd as lsm
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+ALL_LAYOUTS = [("K", "MN"), ("K", "K"), ("MN", "MN"), ("MN", "K")]
+DTYPES = [lsm.GEMM_BF16_F32, lsm.GEMM_BF16_BF16, lsm.GEMM_F16_F16, lsm.GEMM_F16_F32]
+# 4104 x 4088: 17 x 16 tiles of 256 (at least 256, so the ping-pong kernel),
+# ragged in M and N but whole 16-byte chunks along every contiguous extent
+# (else the register-staged kernel serves the shape); K = 264 ends in a
+# partial K tile of 8.
+M, N, K = 4104, 4088, 264
+# ldc 4096: rows 16-byte aligned for every output type (LDS-staged epilogue);
+# ldc 4090: not aligned for any (direct epilogue).
+LDCS = [4096, 4090]
+ROWS = [0, 1, 255, 256, 2047, 4095, 4096, 4103]
+
+
+def takes_pingpong(M, N, K):
+    """The dispatch rule for 16-bit inputs: M > 32, at least 256 tiles of
+    256 x 256, and every contiguous extent a whole number of 16-byte chunks
+    (the 32-bit offset limit is far away at these sizes)."""
+    tiles = -(-M // 256) * -(-N // 256)
+    return M > 32 and tiles >= 256 and all((2 * x) % 16 == 0 for x in (M, N, K))
+
+
+def test_shape_takes_the_pingpong_kernel():
+    assert takes_pingpong(M, N, K)
+    assert not takes_pingpong(4100, 4090, 264)   # ragged chunks: register-staged kernel
+
+
+@pytest.fixture(scope="module")
+def variant():
+    lib = lsm.ablation_library("mfma16")
+    h = lib.gemm_create()
+    yield lib, h
+    lib.gemm_destroy(h)
+
+
+@pytest.mark.parametrize("gd", DTYPES)
+@pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
+def test_mfma16_build_matches_the_library(variant, gd, la, lb):
+    p = H.problem(M, N, K, H.IN_OF[gd], la, lb, "int", (61, 62))
+    want = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
+    want = want.reshape(len(ROWS), N)
+    for ldc in LDCS:
+        print(f"CASE mfma16 {M}x{N}x{K} {la}{lb} dtype {gd} ldc {ldc}", flush=True)
+        lib_out = H.run_gpu(p, gd, ldc=ldc, extra_rows=1)
+        H.assert_canary(lib_out, M, N, gd)
+        H.assert_exact(lib_out[ROWS, :N], want, gd, f"library {la}{lb} ldc {ldc}")
+        got = H.run_gpu(p, gd, ldc=ldc, extra_rows=1, lib=variant)
+        H.assert_canary(got, M, N, gd)
+        bad = np.count_nonzero(got != lib_out)
+        assert bad == 0, f"mfma16 build differs from the library in {bad} entries ({la}{lb}, ldc {ldc})"
+
+
+def test_mfma16_build_real_inputs():
+    """Real-valued operands: within the bf16-output tolerance of the oracle."""
+    lib = lsm.ablation_library("mfma16")
+    h = lib.gemm_create()
+    try:
+        gd = lsm.GEMM_BF16_BF16
+        print(f"CASE mfma16 real {M}x{N}x{K} NN bf16 out", flush=True)
+        p = H.problem(M, N, K, H.IN_OF[gd], "K", "MN", "normal", (63, 64))
+        got = H.run_gpu(p, gd, ldc=4096, lib=(lib, h))
+        ref = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
+        H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma16 real")
+    finally:
+        lib.gemm_destroy(h)

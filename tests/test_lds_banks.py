@@ -113,7 +113,8 @@ def layouts():
         lib = ctypes.CDLL(p)
         for f in ("lsm_kc_chunk_offset", "lsm_mn_chunk_offset", "lsm_loader_lds_offset",
                   "lsm_frag_kc_offset", "lsm_frag_tr_offset", "lsm_layout_swizzled",
-                  "lsm_loader_lds_offset8", "lsm_frag_kc8_offset", "lsm_frag_tr8_offset"):
+                  "lsm_loader_lds_offset8", "lsm_frag_kc8_offset", "lsm_frag_tr8_offset",
+                  "lsm_frag16_kc_offset", "lsm_frag16_tr_offset", "lsm_epi_stage_offset"):
             getattr(lib, f).restype = ctypes.c_int
         libs["swizzled" if s == "" else "linear"] = lib
     assert libs["swizzled"].lsm_layout_swizzled() == 1
@@ -265,3 +266,75 @@ def test_fp8_loader_slots_are_a_permutation(layouts, row_bytes, kc):
 def test_direct_to_lds_writes_are_conflict_free():
     # buffer_load ... lds writes lane L's 16 bytes to slot L of a 1 KiB block
     assert degree([16 * l for l in range(64)], 16) == 1
+
+
+# ------------------------------------------------------------------ 16 x 16 x 32 fragments
+# (the ping-pong kernel's 16 x 16 A/B build: lane l holds row/column l & 15,
+# k = 8*(l >> 4) + 0..7 of each 32-deep k step)
+
+def test_16x16_k_contig_reads_are_conflict_free(layouts):
+    # ds_read_b128: each 16-lane phase reads one logical chunk of 16 rows,
+    # the same access the swizzle serves for the 32 x 32 fragments
+    lib = layouts["swizzled"]
+    for base in range(0, 256, 16):
+        for kk in range(2):
+            addrs = [lib.lsm_frag16_kc_offset(l, base, kk, 128) for l in range(64)]
+            assert degree(addrs, 16) == 1
+
+
+def test_16x16_transposed_reads_are_two_way(layouts):
+    # ds_read_b64_tr_b16 on a 512-byte-row B tile: a 32-lane phase reads
+    # k-rows {k..k+3} and {k+8..k+11}, whose chunks the period-4 swizzle puts
+    # in the same banks, so these reads are 2-way (the 32 x 32 ones are not)
+    lib = layouts["swizzled"]
+    worst = 1
+    for base in range(0, 256, 16):
+        for kk in range(2):
+            for h in range(2):
+                addrs = [lib.lsm_frag16_tr_offset(l, base, kk, h, 512) for l in range(64)]
+                worst = max(worst, degree(addrs, 8))
+    assert worst == 2
+
+
+# ------------------------------------------------------------------ epilogue staging
+# Each wave writes its accumulators, converted, into a row-major region of 64
+# output elements per row, then reads 16 bytes per lane back (one or two rows
+# per 16-lane phase).  Rows and columns per accumulator register follow the
+# MFMA output layouts: 32 x 32: row 8*(r >> 2) + 4*(l >> 5) + (r & 3), column
+# l & 31; 16 x 16: row 4*(l >> 4) + r, column l & 15.
+
+def acc_row_col(mf, r, lane):
+    if mf == 32:
+        return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane & 31
+    return 4 * (lane >> 4) + r, lane & 15
+
+
+@pytest.mark.parametrize("mf", [32, 16])
+@pytest.mark.parametrize("esz", [4, 2])
+def test_epilogue_staging_writes_and_reads_are_conflict_free(layouts, mf, esz):
+    lib = layouts["swizzled"]
+    rowb = 64 * esz
+    off = lambda row, chunk: lib.lsm_epi_stage_offset(row, chunk, rowb, mf)
+    for i in range(64 // mf):            # 64 rows of staged accumulators
+        for j in range(64 // mf):
+            for r in range(16 if mf == 32 else 4):
+                addrs = []
+                for lane in range(64):
+                    row, col = acc_row_col(mf, r, lane)
+                    row, col = row + mf * i, col + mf * j
+                    addrs.append(off(row, col * esz // 16) + (col * esz) % 16)
+                assert degree(addrs, esz) == 1, (i, j, r)
+    cpr = rowb // 16
+    for it in range(64 * cpr // 64):
+        addrs = [off(it * (64 // cpr) + lane // cpr, lane % cpr) for lane in range(64)]
+        assert degree(addrs, 16) == 1
+
+
+@pytest.mark.parametrize("mf", [32, 16])
+@pytest.mark.parametrize("esz", [4, 2])
+def test_epilogue_staging_is_a_permutation_of_each_row(layouts, mf, esz):
+    lib = layouts["swizzled"]
+    rowb = 64 * esz
+    for row in range(64):
+        offs = sorted(lib.lsm_epi_stage_offset(row, c, rowb, mf) for c in range(rowb // 16))
+        assert offs == [row * rowb + 16 * c for c in range(rowb // 16)]
