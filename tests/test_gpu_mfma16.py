@@ -9,7 +9,6 @@ library's own output is checked against the oracle on sampled rows.
 """
 import numpy as np
 import pytest
-import torch
 
 import lds_staged_matrix_amd as lsm
 import gpu_harness as H
@@ -67,16 +66,11 @@ def test_mfma16_build_matches_the_library(variant, gd, la, lb):
         assert bad == 0, f"mfma16 build differs from the library in {bad} entries ({la}{lb}, ldc {ldc})"
 
 
-def test_mfma16_build_real_inputs():
+def test_mfma16_build_real_inputs(variant):
     """Real-valued operands: within the bf16-output tolerance of the oracle."""
-    lib = lsm.ablation_library("mfma16")
-    h = lib.gemm_create()
-    try:
-        gd = lsm.GEMM_BF16_BF16
-        print(f"CASE mfma16 real {M}x{N}x{K} NN bf16 out", flush=True)
-        p = H.problem(M, N, K, H.IN_OF[gd], "K", "MN", "normal", (63, 64))
-        got = H.run_gpu(p, gd, ldc=4096, lib=(lib, h))
-        ref = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
-        H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma16 real")
-    finally:
-        lib.gemm_destroy(h)
+    gd = lsm.GEMM_BF16_BF16
+    print(f"CASE mfma16 real {M}x{N}x{K} NN bf16 out", flush=True)
+    p = H.problem(M, N, K, H.IN_OF[gd], "K", "MN", "normal", (63, 64))
+    got = H.run_gpu(p, gd, ldc=4096, lib=variant)
+    ref = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
+    H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma16 real")
