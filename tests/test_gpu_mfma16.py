@@ -74,3 +74,17 @@ def test_mfma16_build_real_inputs(variant):
     got = H.run_gpu(p, gd, ldc=4096, lib=variant)
     ref = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
     H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma16 real")
+
+
+@pytest.mark.parametrize("k", [0, 8, 64, 72, 128])
+def test_mfma16_build_short_k(variant, k):
+    """The ping-pong prologue's cases: no K tile (C = 0), one K tile (full or
+    partial) and two (the second partial or full), against the library."""
+    gd = lsm.GEMM_BF16_F32
+    print(f"CASE mfma16 short K {M}x{N}x{k}", flush=True)
+    p = H.problem(M, N, k, H.IN_OF[gd], "K", "MN", "int", (65, 66))
+    lib_out = H.run_gpu(p, gd, ldc=4096)
+    got = H.run_gpu(p, gd, ldc=4096, lib=variant)
+    want = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
+    H.assert_exact(lib_out[ROWS, :N], want.reshape(len(ROWS), N), gd, f"library K={k}")
+    assert np.count_nonzero(got != lib_out) == 0, f"mfma16 build differs from the library at K={k}"
