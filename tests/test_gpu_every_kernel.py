@@ -2,10 +2,11 @@
 
 The library instantiates each kernel for every operand layout and element
 type; which one runs depends on the shape class.  Here one shape per class
-runs in all four layouts and with every output type on integer inputs, where
-the result is unique: sampled rows (the first, the last and ones at tile
-edges) and a random sample of entries must equal the oracle's bit for bit,
-and C outside the M x N block must keep its canary.  Each shape is first
+runs in all four layouts and with every output type.  On integer inputs the
+result is unique: sampled rows (the first, the last and ones at tile edges)
+and a random sample of entries must equal the oracle's bit for bit.  On real
+inputs (uniform in [-1, 1]) they must lie within the output type's
+tolerance.  C outside the M x N block must keep its canary.  Each shape is first
 checked to fall in its class by the dispatch rule written out below.
 """
 import ctypes
@@ -78,32 +79,38 @@ CASES8 = [
 ]
 
 
-def check(cls, M, N, K, la, lb, gd, seed):
+def check(cls, M, N, K, la, lb, gd, seed, dist):
     es = 1 if H.IN_OF[gd] == synth.E4M3 else 2
     assert shape_class(M, N, K, la, lb, es) == cls, (cls, M, N, K, la, lb)
-    print(f"CASE every-kernel {cls} {M}x{N}x{K} {la}{lb} dtype {gd}", flush=True)
-    p = H.problem(M, N, K, H.IN_OF[gd], la, lb, "int", (seed, seed + 1))
+    print(f"CASE every-kernel {cls} {M}x{N}x{K} {la}{lb} dtype {gd} {dist}", flush=True)
+    p = H.problem(M, N, K, H.IN_OF[gd], la, lb, dist, (seed, seed + 1))
     C = H.run_gpu(p, gd, extra_rows=1)
     H.assert_canary(C, M, N, gd)
     rows = sorted({0, 1, min(M - 1, 63), min(M - 1, 64), M // 2, M - 2, M - 1})
     want = H.oracle_entries(p, np.repeat(rows, N), np.tile(np.arange(N), len(rows)))
-    H.assert_exact(C[rows, :N], want.reshape(len(rows), N), gd, f"{cls} {la}{lb} rows")
     rng = np.random.default_rng(seed)
     r, c = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
-    H.assert_exact(C[r, c], H.oracle_entries(p, r, c), gd, f"{cls} {la}{lb} sample")
+    if dist == "int":
+        H.assert_exact(C[rows, :N], want.reshape(len(rows), N), gd, f"{cls} {la}{lb} rows")
+        H.assert_exact(C[r, c], H.oracle_entries(p, r, c), gd, f"{cls} {la}{lb} sample")
+    else:
+        H.assert_close(C[rows, :N], want.reshape(len(rows), N), K, gd, f"{cls} {la}{lb} rows")
+        H.assert_close(C[r, c], H.oracle_entries(p, r, c), K, gd, f"{cls} {la}{lb} sample")
 
 
+@pytest.mark.parametrize("dist", ["int", "uniform"])
 @pytest.mark.parametrize("case", CASES16, ids=lambda c: c[0])
 @pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
 @pytest.mark.parametrize("gd", DTYPES16)
-def test_every_16bit_kernel(case, la, lb, gd):
+def test_every_16bit_kernel(case, la, lb, gd, dist):
     cls, M, N, K = case
-    check(cls, M, N, K, la, lb, gd, 700 + 10 * gd)
+    check(cls, M, N, K, la, lb, gd, 700 + 10 * gd, dist)
 
 
+@pytest.mark.parametrize("dist", ["int", "uniform"])
 @pytest.mark.parametrize("case", CASES8, ids=lambda c: c[0])
 @pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
 @pytest.mark.parametrize("gd", DTYPES8)
-def test_every_8bit_kernel(case, la, lb, gd):
+def test_every_8bit_kernel(case, la, lb, gd, dist):
     cls, M, N, K = case
-    check(cls, M, N, K, la, lb, gd, 800 + 10 * gd)
+    check(cls, M, N, K, la, lb, gd, 800 + 10 * gd, dist)
