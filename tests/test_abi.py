@@ -85,7 +85,7 @@ FAKE = ctypes.cast(ctypes.pointer(_FAKE_DEVICE), ctypes.c_void_p)
 A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addresses
 
 
-@pytest.mark.parametrize("args,status", [
+VALIDATION_CASES = [
     # (A, B, C, M, N, K, lda, ldb, ldc, layoutA, layoutB, dtype)
     ((A0, B0, C0, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),       # valid
     ((A0, B0, C0, -1, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),
@@ -124,7 +124,10 @@ A0, B0, C0 = 1 << 20, 2 << 20, 3 << 20     # 16-byte aligned, disjoint fake addr
     ((A0, B0, A0 + 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C in A
     ((A0, B0, B0 - 64, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_INVALID_ARG),  # C over B
     ((A0, B0, A0 + 512, 16, 16, 16, 16, 16, 16, 0, 1, 0), lsm.GEMM_ERR_DEVICE),    # just past A
-])
+]
+
+
+@pytest.mark.parametrize("args,status", VALIDATION_CASES)
 def test_validation(lib, args, status):
     assert lsm.gemm_run(FAKE, *args) == status
 
