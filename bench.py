@@ -127,68 +127,6 @@ def cpu_baseline(p, rows):
                       f"{p.M}x{p.N}x{p.K} problem ({rows * p.N} outputs), {dt:.2f} s wall"}
 
 
-def vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p, steps, warmup, stream):
-    """Same operands, same launch counts: hipBLASLt (through torch) against
-    this library, both with 16-bit output.  16-bit inputs: torch.matmul on
-    row-major A[M,K] @ B[K,N] (A K-contiguous, B N-contiguous).  E4M3 inputs:
-    torch._scaled_mm with unit scales, which takes B K-contiguous, so both
-    sides read the workload's B bytes as a K-contiguous B (layout NT) and
-    write bf16.  A reference point only; nothing in the library calls torch."""
-    import torch
-    if tuple(layout) != ("K", "MN") or p.lda != K or p.ldb != N:
-        return None
-    fp8 = w["dtype"] == synth.E4M3
-    if fp8:
-        if N != K:
-            return None                    # B's bytes reread as K-contiguous B need N == K
-        At = A.view(torch.float8_e4m3fn).view(M, K)
-        Bt = B.view(torch.float8_e4m3fn).view(N, K)
-        one = torch.ones((), device="cuda")
-        Ct = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-        gd = DTYPE_CODE[(synth.E4M3, "bf16")]
-
-        def ours():
-            lib.gemm_run(h, A, B, Ct, M, N, K, K, K, N, 0, 0, gd, stream)
-
-        def theirs():
-            torch._scaled_mm(At, Bt.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
-    else:
-        tdt = torch.bfloat16 if w["dtype"] == synth.BF16 else torch.float16
-        gd = DTYPE_CODE[(w["dtype"], "bf16" if w["dtype"] == synth.BF16 else "f16")]
-        At, Bt = A.view(tdt).view(M, K), B.view(tdt).view(K, N)
-        Ct = torch.empty(M, N, dtype=tdt, device="cuda")
-
-        def ours():
-            lib.gemm_run(h, A, B, Ct, M, N, K, p.lda, p.ldb, N, 0, 1, gd, stream)
-
-        def theirs():
-            torch.matmul(At, Bt, out=Ct)
-
-    def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(steps):
-            fn()
-        e0.record(stream)
-        torch.cuda.synchronize()
-        return s0.elapsed_time(e0) / steps
-
-    res = {}
-    for name, fn in (("hipblaslt", theirs), ("library", ours), ("hipblaslt_again", theirs)):
-        t0 = time.time()
-        ms = timed(fn)
-        log(f"vs-hipblaslt {name}: {ms:.5f} ms, wall clock {t0:.1f} .. {time.time():.1f}")
-        res[name + "_ms"] = round(ms, 5)
-        res[name + "_tflops"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
-    res["output"] = "f16" if w["dtype"] == synth.F16 else "bf16"
-    if fp8:
-        res["layout"] = "NT"
-    return res
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +135,9 @@ def main():
     # chip needs ~80 ms of load before its clock settles.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--settle-ms", type=float, default=600.0,
+                    help="before the W warm-up steps, run untimed steps for at least this "
+                         "much wall time so the clock has settled under load (0: none)")
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layout", default=None, help="e.g. K,MN (A contiguity, B contiguity)")
     ap.add_argument("--shape", default=None,
@@ -214,9 +155,6 @@ def main():
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
-    ap.add_argument("--vs-hipblaslt", action="store_true",
-                    help="also time torch.matmul (hipBLASLt) and this library with 16-bit "
-                         "output on the same operands (A K-contiguous, B N-contiguous only)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
@@ -274,6 +212,19 @@ def main():
         log("profile run: 5 launches done")
         return
 
+    # Clock settle: under sustained MFMA load the power controller takes
+    # tens of milliseconds to bring the clock to its steady level, so a few
+    # warm-up steps alone leave the timed steps on a clock that is still
+    # moving.  Untimed steps are run, synchronising every 20, until
+    # `settle_ms` of wall time have passed; then the W warm-up steps.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -294,7 +245,6 @@ def main():
 
     flops = 2.0 * M * N * K
     out_bytes = 4 if w["out"] == "f32" else 2
-    alg_bytes = 2.0 * (M * K + K * N) + out_bytes * M * N
     in_bytes = 1 if w["dtype"] == synth.E4M3 else 2
     alg_bytes = in_bytes * (M * K + K * N) + out_bytes * M * N
     peak_tflops = PEAK_FP8_TFLOPS if w["dtype"] == synth.E4M3 else PEAK_BF16_TFLOPS
@@ -389,7 +339,8 @@ def main():
                    "kernel_ms_mean": round(kavg, 5), "kernel_ms_flushed_median":
                        round(float(np.median(fl_ms)), 5) if fl_ms else None,
                    "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
-                   "kernel_source_hash": src_hash},
+                   "kernel_source_hash": src_hash,
+                   "settle_steps": settle_steps, "settle_ms": round(settle_ms, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -400,9 +351,6 @@ def main():
     if args.variant:
         line["config"]["ablation_build"] = args.variant
         roof["traffic"] = None
-    if args.vs_hipblaslt:
-        line["config"]["vs_hipblaslt"] = vs_hipblaslt(lib, h, w, layout, A, B, M, N, K, p,
-                                                      args.steps, args.warmup, stream)
     lib.gemm_destroy(h)
     print(json.dumps(line), flush=True)
 

@@ -29,6 +29,8 @@ def test_bench_prints_one_complete_json_line():
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
     assert d["unit"] == "TFLOP/s" and d["dtype"] == "bf16" and d["data"] == "synthetic"
     assert "workload" in d["config"]
+    # the clock-settle phase ran before the warm-up steps
+    assert d["config"]["settle_steps"] > 0 and d["config"]["settle_ms"] >= 600
     roof = d["roofline"]
     assert roof["bound"] in ("hbm", "mfma") and roof["unit"] in ("GB/s", "TFLOP/s")
     assert roof["achieved"] > 0 and roof["peak"] > 0
@@ -37,22 +39,3 @@ def test_bench_prints_one_complete_json_line():
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert cpu["unit"] == "TFLOP/s" and cpu["sample"]
-
-
-@pytest.mark.parametrize("workload,output", [("f16_1500x1152x896_nn_f16", "f16"),
-                                             ("e4m3_8192_nn_f32", "bf16")])
-def test_bench_vs_hipblaslt_reports_both_sides(workload, output):
-    """The hipBLASLt reference point: both sides timed on the same operands."""
-    print(f"CASE bench.py --workload {workload} --vs-hipblaslt --steps 3 --warmup 3", flush=True)
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
-                        "--steps", "3", "--warmup", "3", "--no-cpu-baseline", "--no-graph",
-                        "--no-flushed", "--vs-hipblaslt"],
-                       capture_output=True, text=True, timeout=300, cwd=ROOT)
-    assert r.returncode == 0, r.stderr[-2000:]
-    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
-    v = d["config"]["vs_hipblaslt"]
-    assert v is not None and v["output"] == output
-    for side in ("hipblaslt", "library", "hipblaslt_again"):
-        assert v[side + "_ms"] > 0 and v[side + "_tflops"] > 0
-    if workload.startswith("e4m3"):
-        assert v["layout"] == "NT"
