@@ -30,7 +30,7 @@ VARIANTS = {
     "noxcd": ["-DLSM_XCD_REMAP=0"],         # tiles in hardware workgroup order, not grouped per XCD
     "stage1": ["-DLSM_DMA_STAGES=1"],       # 128/64 direct-to-LDS kernel with one LDS stage, no overlap
     "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
-    "mfma16": ["-DLSM_PP_MFMA=16"],         # 16-bit ping-pong kernel on 16x16x32 instead of 32x32x16 MFMAs
+    "mfma32": ["-DLSM_PP_MFMA=32"],         # 16-bit ping-pong kernel on 32x32x16 instead of 16x16x32 MFMAs
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

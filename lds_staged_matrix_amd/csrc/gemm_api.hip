@@ -67,11 +67,12 @@ struct Args {
 // DMA4: the direct-to-LDS kernel with four LDS stages (operand panels beyond the L2).
 enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3, DMA4 = 4 };
 
-// LSM_PP_MFMA = 16 builds the ping-pong kernel's 16-bit instances with
-// v_mfma_f32_16x16x32 instead of v_mfma_f32_32x32x16; it exists only for the
-// A/B build that measures the MFMA shape.  The library is built with 32.
+// The ping-pong kernel's 16-bit instances run on v_mfma_f32_16x16x32.
+// LSM_PP_MFMA = 32 builds them with v_mfma_f32_32x32x16 instead; it exists
+// only for the A/B build that measures the MFMA shape.  The library is built
+// with 16.
 #ifndef LSM_PP_MFMA
-#define LSM_PP_MFMA 32
+#define LSM_PP_MFMA 16
 #endif
 
 template <class T, int KIND, int LA, int LB, int IN, int OUT>

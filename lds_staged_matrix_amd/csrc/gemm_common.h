@@ -67,11 +67,15 @@ struct Tile {
 // MN elements.  "outer" is the strided dimension of the operand in memory,
 // "inner" its unit-stride dimension; ES is the element size in bytes.  The
 // tile is filled in rounds of NT 16-byte chunks: chunk id = thread + round *
-// NT, numbered row-major.
-template <int MN, int BK, int LAYOUT, int NT, int ES_ = 2>
+// NT, numbered row-major.  MF16 = 1 lays an MN-contiguous 16-bit tile out for
+// the transposed fragments of the 16 x 16 x 32 MFMA (mn16_chunk_offset);
+// otherwise, and for K-contiguous tiles, the layout is the one the 32 x 32
+// fragments read (kc_chunk_offset, mn_chunk_offset).
+template <int MN, int BK, int LAYOUT, int NT, int ES_ = 2, int MF16_ = 0>
 struct OperandTile {
   static constexpr bool kcontig = LAYOUT == KC;
   static constexpr int ES = ES_;
+  static constexpr bool mf16 = MF16_ != 0 && !kcontig;          // 16 x 16 x 32 MN layout
   static constexpr int ROWS = kcontig ? MN : BK;                 // outer extent
   static constexpr int INNER = kcontig ? BK : MN;                // inner extent (elements)
   static constexpr int ROW_BYTES = ES * INNER;
@@ -81,10 +85,21 @@ struct OperandTile {
   static constexpr int CHUNKS = BYTES / 16;
   static constexpr int LOADS = CHUNKS / NT;                      // 16-byte loads per thread
   static constexpr int ROW_STEP = NT / CPR;                      // rows between a thread's loads
-  static constexpr int SWZ_PERIOD = kcontig ? 16 : (ES == 2 ? 4 : 8);   // rows per swizzle period
+  static constexpr int SWZ_PERIOD = kcontig ? 16 : mf16 ? 16 : (ES == 2 ? 4 : 8);   // rows per swizzle period
+  // A thread's chunks of every load round share one swizzle phase when the
+  // round step is a multiple of the period (one lane offset for all rounds);
+  // the 16 x 16 x 32 MN layout with 8-row rounds alternates two phases (one
+  // lane offset for even and one for odd rounds).
+  static constexpr int LANE_OFFSETS = ROW_STEP % SWZ_PERIOD == 0 ? 1 : 2;
+  static_assert(!mf16 || ES == 2, "the 16 x 16 x 32 layout is for 16-bit elements");
   static_assert(CHUNKS % NT == 0, "tile must split evenly into 16-byte loads");
-  static_assert(NT % CPR == 0 && ROW_STEP % SWZ_PERIOD == 0,
-                "a thread's chunks must share one swizzle phase");
+  static_assert(NT % CPR == 0 && (ROW_STEP % SWZ_PERIOD == 0 || 2 * ROW_STEP == SWZ_PERIOD),
+                "a thread's chunks must take one or two swizzle phases");
+  // XOR applied to the chunk index of row `row` of this tile.
+  __host__ __device__ static constexpr int swizzle(int row) {
+    return kcontig ? kc_swizzle(row, ROW_BYTES)
+                   : mf16 ? mn16_swizzle(row, ROW_BYTES) : mn_swizzle(row, ROW_BYTES, ES);
+  }
 };
 
 template <int IN>
@@ -204,18 +219,30 @@ __device__ __forceinline__ v8i16 read_frag16(const char *lds, int lane, int base
   if constexpr (OT::kcontig) {
     return *(const v8i16 *)(lds + frag16_kc_offset(lane, base, kk, OT::ROW_BYTES));
   } else if constexpr (!LSM_TR_READ) {
+    static_assert(OT::mf16, "16 x 16 x 32 MN layout");
     const int col = base + (lane & 15);
     v8i16 f;
 #pragma unroll
     for (int i = 0; i < 8; i++)
-      f[i] = *(const short *)(lds + mn_chunk_offset(32 * kk + 8 * (lane >> 4) + i, col / 8,
-                                                    OT::ROW_BYTES) + 2 * (col & 7));
+      f[i] = *(const short *)(lds + mn16_chunk_offset(32 * kk + 8 * (lane >> 4) + i, col / 8,
+                                                      OT::ROW_BYTES) + 2 * (col & 7));
     return f;
   } else {
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(lds + frag16_tr_offset(lane, base, kk, 0, OT::ROW_BYTES)));
+    // lds + frag16_tr_offset(lane, base, kk, h, ROW_BYTES), computed as
+    // ((tile + 256*(base >> 7) + lane part) XOR 32*((base >> 4) & 7)) + the
+    // k-step and half, which equals it because the tile base (a multiple of
+    // 1 KiB: every stage and operand tile is) has bits 5-7 clear.  The tile
+    // base changes with the LDS stage, so the XOR is evaluated per read
+    // instead of one loop-invariant address register per fragment.
+    static_assert(OT::mf16 && OT::ROW_BYTES >= 256 && OT::BYTES % 1024 == 0,
+                  "16 x 16 x 32 MN layout, rows of 256 bytes or more");
+    const uint32_t tile = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
+    const uint32_t a = ((tile + 256 * (base >> 7) + (uint32_t)frag16_tr_lane(lane, OT::ROW_BYTES)) ^
+                        (uint32_t)(32 * ((base >> 4) & 7))) +
+                       (uint32_t)(32 * kk * OT::ROW_BYTES);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(uintptr_t)a);
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(lds + frag16_tr_offset(lane, base, kk, 1, OT::ROW_BYTES)));
+        (lds_v4i16 *)(uintptr_t)(a + 4 * OT::ROW_BYTES));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }

@@ -36,10 +36,16 @@
 // handling through buffer range checks and the inline-assembly loads are
 // those of gemm_kernel_dma.h.
 //
-// MF selects the MFMA shape: 32 (v_mfma_f32_32x32x16, and the fp8
-// 32x32x64; the library) or 16 (v_mfma_f32_16x16x32 on 16-bit inputs, an A/B
-// build only: each wave's 128 x 64 block as 8 x 4 blocks of 16 x 16, twice the
-// fragment reads per flop, and the same loads, barriers and LDS layout).
+// MF selects the MFMA shape: 16 (v_mfma_f32_16x16x32, the library's 16-bit
+// instances: each wave's 128 x 64 block as 8 x 4 blocks of 16 x 16) or 32
+// (v_mfma_f32_32x32x16, an A/B build only, and the fp8 32x32x64 of the
+// library's 8-bit instances).  Both read the same LDS bytes per K tile.  On
+// MI355X, at its 1400 W socket limit on random operands, the 16 x 16 x 32
+// instruction spends less energy per flop (a quarter of the accumulator
+// register traffic per instruction for half the work), so the chip holds a
+// higher clock: 8192^3 bf16 runs about 5% faster with it.  Its transposed
+// reads need their own swizzle (mn16_swizzle in lds_layout.h), with a period
+// of two load rounds.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,8 +79,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   constexpr int ES = InT<IN>::ES;
   constexpr int KSTEPS = T::BK / (MF == 32 ? InT<IN>::KSTEP : 32);   // MFMA k-steps per K tile
   constexpr int FM = T::TM / MF, FN = T::TN / MF;        // MFMA blocks per wave
-  using OA = OperandTile<T::BM, T::BK, LA, LOADERS, ES>;
-  using OB = OperandTile<T::BN, T::BK, LB, LOADERS, ES>;
+  // With 16 x 16 x 32 MFMAs an MN-contiguous tile takes the layout of those
+  // fragments' transposed reads; its swizzle period is two load rounds.
+  using OA = OperandTile<T::BM, T::BK, LA, LOADERS, ES, MF == 16>;
+  using OB = OperandTile<T::BN, T::BK, LB, LOADERS, ES, MF == 16>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int LOADS_PER_TILE = OA::LOADS + OB::LOADS;  // per group-0 wave
   constexpr int FRAGS = KSTEPS * (FM + FN);               // fragment reads per memory phase
@@ -95,40 +103,48 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
 
   // Loader geometry for group 0 (tid < LOADERS).
-  int a_inner, b_inner;
+  int a_inner, b_inner, unused;
   const uint32_t a_voff = dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, a_inner);
   const uint32_t b_voff = dma_lane_offset<OB>(tid & (LOADERS - 1), n0, N, ldb, b_bytes, b_inner);
+  // offsets of the odd load rounds (the same as the even ones unless the
+  // tile's swizzle period is two rounds)
+  const uint32_t a_voff1 = OA::LANE_OFFSETS == 2
+      ? dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, unused, 1) : a_voff;
+  const uint32_t b_voff1 = OB::LANE_OFFSETS == 2
+      ? dma_lane_offset<OB>(tid & (LOADERS - 1), n0, N, ldb, b_bytes, unused, 1) : b_voff;
   const uint32_t a_round = (uint32_t)(OA::ROW_STEP * lda * ES);
   const uint32_t b_round = (uint32_t)(OB::ROW_STEP * ldb * ES);
   const uint32_t a_kstep = (uint32_t)(LA == KC ? ES * T::BK : ES * T::BK * lda);
   const uint32_t b_kstep = (uint32_t)(LB == KC ? ES * T::BK : ES * T::BK * ldb);
   const int lwave = wave & 3;
 
-  // Byte offsets of this wave's loads of K tile kt (round i of A is load i,
-  // round i of B is load OA::LOADS + i).
-  auto voffs = [&](int kt, uint32_t &av, uint32_t &bv) {
+  // Load d of K tile kt is round d of A (d < OA::LOADS) or round
+  // d - OA::LOADS of B.  Per K tile, the lane offsets of each operand's even
+  // and odd load rounds (a K-contiguous tile has one phase, and its chunks at
+  // k >= K in the last, partial K tile read as zero through kOutOfRange).
+  struct Voffs { uint32_t a[2], b[2]; };
+  auto voffs = [&](int kt) {
     const int k0 = kt * T::BK;
-    av = a_voff;
-    bv = b_voff;
-    if (k0 + T::BK > K) {   // last, partial K tile: chunks at k >= K read as zero
-      if constexpr (LA == KC) av = k0 + a_inner < K ? a_voff : kOutOfRange;
-      if constexpr (LB == KC) bv = k0 + b_inner < K ? b_voff : kOutOfRange;
+    Voffs v{{a_voff, a_voff1}, {b_voff, b_voff1}};
+    if (k0 + T::BK > K) {
+      if constexpr (LA == KC) v.a[0] = v.a[1] = k0 + a_inner < K ? a_voff : kOutOfRange;
+      if constexpr (LB == KC) v.b[0] = v.b[1] = k0 + b_inner < K ? b_voff : kOutOfRange;
     }
+    return v;
   };
-  auto issue_one = [&](int kt, int d, uint32_t av, uint32_t bv) {
+  auto issue_one = [&](int kt, int d, const Voffs &v) {
     const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
     if (d < OA::LOADS)
-      dma16(rsA, st + (uint32_t)((d * LOADERS + 64 * lwave) * 16), av,
+      dma16(rsA, st + (uint32_t)((d * LOADERS + 64 * lwave) * 16), v.a[d & 1],
             (uint32_t)kt * a_kstep + d * a_round);
     else
-      dma16(rsB, st + OA::BYTES + (uint32_t)(((d - OA::LOADS) * LOADERS + 64 * lwave) * 16), bv,
-            (uint32_t)kt * b_kstep + (d - OA::LOADS) * b_round);
+      dma16(rsB, st + OA::BYTES + (uint32_t)(((d - OA::LOADS) * LOADERS + 64 * lwave) * 16),
+            v.b[(d - OA::LOADS) & 1], (uint32_t)kt * b_kstep + (d - OA::LOADS) * b_round);
   };
   auto issue = [&](int kt) {
-    uint32_t av, bv;
-    voffs(kt, av, bv);
+    const Voffs v = voffs(kt);
 #pragma unroll
-    for (int d = 0; d < LOADS_PER_TILE; d++) issue_one(kt, d, av, bv);
+    for (int d = 0; d < LOADS_PER_TILE; d++) issue_one(kt, d, v);
   };
 
   typename L::type acc[FM][FN];
@@ -166,8 +182,8 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
       // `with_loads` compiles the load issue in; `load` then decides at run time.
       auto m_phase = [&](auto with_loads, bool load) {
         constexpr bool LOAD = decltype(with_loads)::value;
-        uint32_t av = 0, bv = 0;
-        if constexpr (LOAD) voffs(kt + 1, av, bv);
+        Voffs v{};
+        if constexpr (LOAD) v = voffs(kt + 1);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
@@ -189,23 +205,20 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
               if (load) {
 #pragma unroll
                 for (int d = q * LOADS_PER_TILE / FRAGS; d < (q + 1) * LOADS_PER_TILE / FRAGS; d++)
-                  issue_one(kt + 1, d, av, bv);
+                  issue_one(kt + 1, d, v);
               }
             }
           }
         }
       };
+      // Two copies of the phase, with and without the loads: a run-time
+      // branch around each load would make the compiler wait for every
+      // outstanding fragment read at each branch.
       const bool load_next = group == 0 && kt >= 1 && kt + 1 < KT;
-      if constexpr (MF == 32) {
-        if (load_next)
-          m_phase(std::true_type{}, true);
-        else
-          m_phase(std::false_type{}, false);
-      } else {
-        // one copy of the phase, a uniform branch per load: with a second copy
-        // the 16 x 16 build runs out of registers and spills
-        m_phase(std::true_type{}, load_next);
-      }
+      if (load_next)
+        m_phase(std::true_type{}, true);
+      else
+        m_phase(std::false_type{}, false);
       wait_lds_reads();
       wg_barrier();                                      // end of M(kt)
 

@@ -27,6 +27,12 @@ int lsm_frag16_kc_offset(int lane, int base, int kk, int row_bytes) {
 int lsm_frag16_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
   return lsm::frag16_tr_offset(lane, base, kk, h, row_bytes);
 }
+int lsm_mn16_swizzle(int k, int row_bytes) { return lsm::mn16_swizzle(k, row_bytes); }
+int lsm_mn16_chunk_offset(int k, int chunk, int row_bytes) {
+  return lsm::mn16_chunk_offset(k, chunk, row_bytes);
+}
+int lsm_loader_lds_offset16(int id, int row_bytes) { return lsm::loader_lds_offset16(id, row_bytes); }
+int lsm_frag16_tr_lane(int lane, int row_bytes) { return lsm::frag16_tr_lane(lane, row_bytes); }
 int lsm_epi_stage_offset(int row, int chunk, int row_bytes, int mf) {
   return lsm::epi_stage_offset(row, chunk, row_bytes, mf);
 }

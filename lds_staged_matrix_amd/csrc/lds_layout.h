@@ -75,6 +75,19 @@ __host__ __device__ constexpr int mn_swizzle(int k, int row_bytes, int es = 2) {
                                                           : (row_bytes == 64 ? 2 * ((k >> 2) & 1) : 0));
 }
 
+// XOR applied to the chunk index of k-row `k` of an MN-contiguous tile of
+// 16-bit elements read by the transposed fragments of v_mfma_f32_16x16x32.
+// Those fragments hold k = 8g .. 8g+7 in lane group g (16 lanes), so one
+// 32-lane phase of ds_read_b64_tr_b16 reads k-rows {k..k+3} and {k+8..k+11},
+// 32 bytes each.  For rows of 256 bytes or more every row starts at the same
+// bank, and the XOR (k & 3) | ((k >> 1) & 4), on chunk bits 1-3, puts those
+// eight rows in the eight distinct 32-byte eighths of the bank line.  Its
+// period in k is 16, so a loader whose rounds are 8 rows apart needs one lane
+// offset for even and one for odd rounds.
+__host__ __device__ constexpr int mn16_swizzle(int k, int row_bytes) {
+  return (!LSM_LDS_SWIZZLE || row_bytes < 256) ? 0 : 2 * ((k & 3) | ((k >> 1) & 4));
+}
+
 // Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
 __host__ __device__ constexpr int kc_chunk_offset(int row, int chunk, int row_bytes) {
   return row * row_bytes + 16 * (chunk ^ kc_swizzle(row, row_bytes));
@@ -83,6 +96,12 @@ __host__ __device__ constexpr int kc_chunk_offset(int row, int chunk, int row_by
 // Byte offset of 16-byte chunk `chunk` of k-row `k` in an MN-contiguous tile.
 __host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_bytes, int es = 2) {
   return k * row_bytes + 16 * (chunk ^ mn_swizzle(k, row_bytes, es));
+}
+
+// Byte offset of 16-byte chunk `chunk` of k-row `k` in an MN-contiguous tile
+// laid out for the 16 x 16 x 32 transposed reads.
+__host__ __device__ constexpr int mn16_chunk_offset(int k, int chunk, int row_bytes) {
+  return k * row_bytes + 16 * (chunk ^ mn16_swizzle(k, row_bytes));
 }
 
 // ---------------------------------------------------------------- loader
@@ -97,6 +116,11 @@ __host__ __device__ constexpr int loader_chunk(int id, int row_bytes) { return i
 __host__ __device__ constexpr int loader_lds_offset(int id, int row_bytes, bool k_contig, int es = 2) {
   return k_contig ? kc_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes)
                   : mn_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes, es);
+}
+
+// The same for an MN-contiguous 16-bit tile in the 16 x 16 x 32 layout.
+__host__ __device__ constexpr int loader_lds_offset16(int id, int row_bytes) {
+  return mn16_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes);
 }
 
 // ---------------------------------------------------------------- fragment reads
@@ -121,23 +145,42 @@ __host__ __device__ constexpr int frag_tr_offset(int lane, int base, int kk, int
          8 * (lane & 1);
 }
 
-// Fragments of v_mfma_f32_16x16x32_{bf16,f16}, used by the 16 x 16 A/B build
-// of the ping-pong kernel (its results, bit-exact on integer inputs in every
-// layout, confirm the layout): lane l holds operand row/column (l & 15) and
+// Fragments of v_mfma_f32_16x16x32_{bf16,f16}, used by the ping-pong kernel
+// on 16-bit inputs: lane l holds operand row/column (l & 15) and
 // k = 8*(l >> 4) + i, i = 0..7; `kk` is the 32-deep k step inside the tile.
+// `base`, the fragment's first row/column in the tile, is a multiple of 16.
+// Both offsets are written as a lane-dependent part plus a part that depends
+// only on `base` and `kk`, so that in an unrolled loop the compiler keeps a
+// few lane constants and folds the rest into the instructions' immediates.
 
-// K-contiguous operand: one ds_read_b128 per fragment.
+// K-contiguous operand: one ds_read_b128 per fragment, row base + (l & 15),
+// chunk 4*kk + (l >> 4).  Every K-contiguous swizzle has a period in the row
+// that divides 16, so the row's swizzle is that of row (l & 15).
 __host__ __device__ constexpr int frag16_kc_offset(int lane, int base, int kk, int row_bytes) {
-  return kc_chunk_offset(base + (lane & 15), 4 * kk + (lane >> 4), row_bytes);
+  return base * row_bytes + kc_chunk_offset(lane & 15, 4 * kk + (lane >> 4), row_bytes);
 }
 
-// MN-contiguous operand: two ds_read_b64_tr_b16 per fragment, half h = 0, 1
+// MN-contiguous operand in the 16 x 16 x 32 layout (mn16_chunk_offset, rows
+// of 256 bytes or more): two ds_read_b64_tr_b16 per fragment, half h = 0, 1
 // delivering k = 8*(l >> 4) + 4*h + 0..3.  Source lane l reads k-row
-// 32*kk + 8*(l >> 4) + 4*h + ((l >> 2) & 3) at columns base + 4*(l & 3) .. +3.
-__host__ __device__ constexpr int frag16_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
-  return mn_chunk_offset(32 * kk + 8 * (lane >> 4) + 4 * h + ((lane >> 2) & 3),
-                         (base + 4 * (lane & 3)) / 8, row_bytes) +
+// k = 32*kk + 8*(l >> 4) + 4*h + ((l >> 2) & 3) at columns base + 4*(l & 3) .. +3,
+// i.e. chunk c = 2f + ((l & 3) >> 1) with f = base / 16, bytes 8*(l & 1) .. +7.
+// mn16_swizzle(k) = 2s, with s = (k & 3) | ((k >> 1) & 4) a function of the
+// lane alone, so the swizzled chunk is 2(f ^ s) + ((l & 3) >> 1), and with
+// f = 8 fw + fi (fi < 8) the offset is
+//   32*8*fw + (frag16_tr_lane(l) XOR 32*fi) + (32*kk + 4*h)*row_bytes,
+// where the lane part holds the k-row, the byte within the chunk pair and
+// 32*s in bits 5-7.  The kernel adds the lane part to a stage base whose bits
+// 5-7 are zero and applies the XOR to the sum, so one register per operand
+// serves every fragment.
+__host__ __device__ constexpr int frag16_tr_lane(int lane, int row_bytes) {
+  const int k0 = 8 * (lane >> 4) + ((lane >> 2) & 3);      // the k-row, less 32*kk + 4*h
+  return k0 * row_bytes + 32 * (mn16_swizzle(k0, row_bytes) >> 1) + 16 * ((lane & 3) >> 1) +
          8 * (lane & 1);
+}
+__host__ __device__ constexpr int frag16_tr_offset(int lane, int base, int kk, int h, int row_bytes) {
+  return 256 * (base >> 7) + (frag16_tr_lane(lane, row_bytes) ^ (32 * ((base >> 4) & 7))) +
+         (32 * kk + 4 * h) * row_bytes;
 }
 
 // Fragments of v_mfma_scale_f32_32x32x64_f8f6f4 on 8-bit elements (checked

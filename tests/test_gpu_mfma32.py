@@ -1,11 +1,12 @@
-"""The A/B build of the ping-pong kernel on v_mfma_f32_16x16x32 (build
-variant "mfma16"), against the library and the oracle.
+"""The A/B build of the ping-pong kernel on v_mfma_f32_32x32x16 (build
+variant "mfma32"), against the library (v_mfma_f32_16x16x32) and the oracle.
 
 The build changes only the MFMA shape of the 16-bit ping-pong kernel: its
-fragment reads, accumulator layout and both epilogues (the LDS-staged one,
-taken when C rows are 16-byte aligned, and the direct one).  On integer inputs
-the result is unique, so it must equal the library's bit for bit; the
-library's own output is checked against the oracle on sampled rows.
+LDS layout of MN-contiguous tiles (the transposed-read swizzle of each
+fragment shape), fragment reads, accumulator layout and both epilogues (the
+LDS-staged one, taken when C rows are 16-byte aligned, and the direct one).
+On integer inputs the result is unique, so the two must agree bit for bit;
+the library's own output is checked against the oracle on sampled rows.
 """
 import numpy as np
 import pytest
@@ -43,7 +44,7 @@ def test_shape_takes_the_pingpong_kernel():
 
 @pytest.fixture(scope="module")
 def variant():
-    lib = lsm.ablation_library("mfma16")
+    lib = lsm.ablation_library("mfma32")
     h = lib.gemm_create()
     yield lib, h
     lib.gemm_destroy(h)
@@ -51,40 +52,40 @@ def variant():
 
 @pytest.mark.parametrize("gd", DTYPES)
 @pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
-def test_mfma16_build_matches_the_library(variant, gd, la, lb):
+def test_mfma32_build_matches_the_library(variant, gd, la, lb):
     p = H.problem(M, N, K, H.IN_OF[gd], la, lb, "int", (61, 62))
     want = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
     want = want.reshape(len(ROWS), N)
     for ldc in LDCS:
-        print(f"CASE mfma16 {M}x{N}x{K} {la}{lb} dtype {gd} ldc {ldc}", flush=True)
+        print(f"CASE mfma32 {M}x{N}x{K} {la}{lb} dtype {gd} ldc {ldc}", flush=True)
         lib_out = H.run_gpu(p, gd, ldc=ldc, extra_rows=1)
         H.assert_canary(lib_out, M, N, gd)
         H.assert_exact(lib_out[ROWS, :N], want, gd, f"library {la}{lb} ldc {ldc}")
         got = H.run_gpu(p, gd, ldc=ldc, extra_rows=1, lib=variant)
         H.assert_canary(got, M, N, gd)
         bad = np.count_nonzero(got != lib_out)
-        assert bad == 0, f"mfma16 build differs from the library in {bad} entries ({la}{lb}, ldc {ldc})"
+        assert bad == 0, f"mfma32 build differs from the library in {bad} entries ({la}{lb}, ldc {ldc})"
 
 
-def test_mfma16_build_real_inputs(variant):
+def test_mfma32_build_real_inputs(variant):
     """Real-valued operands: within the bf16-output tolerance of the oracle."""
     gd = lsm.GEMM_BF16_BF16
-    print(f"CASE mfma16 real {M}x{N}x{K} NN bf16 out", flush=True)
+    print(f"CASE mfma32 real {M}x{N}x{K} NN bf16 out", flush=True)
     p = H.problem(M, N, K, H.IN_OF[gd], "K", "MN", "normal", (63, 64))
     got = H.run_gpu(p, gd, ldc=4096, lib=variant)
     ref = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
-    H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma16 real")
+    H.assert_close(got[ROWS, :N], ref.reshape(len(ROWS), N), K, gd, "mfma32 real")
 
 
 @pytest.mark.parametrize("k", [0, 8, 64, 72, 128])
-def test_mfma16_build_short_k(variant, k):
+def test_mfma32_build_short_k(variant, k):
     """The ping-pong prologue's cases: no K tile (C = 0), one K tile (full or
     partial) and two (the second partial or full), against the library."""
     gd = lsm.GEMM_BF16_F32
-    print(f"CASE mfma16 short K {M}x{N}x{k}", flush=True)
+    print(f"CASE mfma32 short K {M}x{N}x{k}", flush=True)
     p = H.problem(M, N, k, H.IN_OF[gd], "K", "MN", "int", (65, 66))
     lib_out = H.run_gpu(p, gd, ldc=4096)
     got = H.run_gpu(p, gd, ldc=4096, lib=variant)
     want = H.oracle_entries(p, np.repeat(ROWS, N), np.tile(np.arange(N), len(ROWS)))
     H.assert_exact(lib_out[ROWS, :N], want.reshape(len(ROWS), N), gd, f"library K={k}")
-    assert np.count_nonzero(got != lib_out) == 0, f"mfma16 build differs from the library at K={k}"
+    assert np.count_nonzero(got != lib_out) == 0, f"mfma32 build differs from the library at K={k}"

@@ -114,7 +114,9 @@ def layouts():
         for f in ("lsm_kc_chunk_offset", "lsm_mn_chunk_offset", "lsm_loader_lds_offset",
                   "lsm_frag_kc_offset", "lsm_frag_tr_offset", "lsm_layout_swizzled",
                   "lsm_loader_lds_offset8", "lsm_frag_kc8_offset", "lsm_frag_tr8_offset",
-                  "lsm_frag16_kc_offset", "lsm_frag16_tr_offset", "lsm_epi_stage_offset"):
+                  "lsm_frag16_kc_offset", "lsm_frag16_tr_offset", "lsm_epi_stage_offset",
+                  "lsm_mn16_swizzle", "lsm_mn16_chunk_offset", "lsm_loader_lds_offset16",
+                  "lsm_frag16_tr_lane"):
             getattr(lib, f).restype = ctypes.c_int
         libs["swizzled" if s == "" else "linear"] = lib
     assert libs["swizzled"].lsm_layout_swizzled() == 1
@@ -269,31 +271,138 @@ def test_direct_to_lds_writes_are_conflict_free():
 
 
 # ------------------------------------------------------------------ 16 x 16 x 32 fragments
-# (the ping-pong kernel's 16 x 16 A/B build: lane l holds row/column l & 15,
+# (the ping-pong kernel on 16-bit inputs: lane l holds row/column l & 15,
 # k = 8*(l >> 4) + 0..7 of each 32-deep k step)
 
 def test_16x16_k_contig_reads_are_conflict_free(layouts):
     # ds_read_b128: each 16-lane phase reads one logical chunk of 16 rows,
     # the same access the swizzle serves for the 32 x 32 fragments
     lib = layouts["swizzled"]
-    for base in range(0, 256, 16):
-        for kk in range(2):
-            addrs = [lib.lsm_frag16_kc_offset(l, base, kk, 128) for l in range(64)]
-            assert degree(addrs, 16) == 1
+    for rb, rows in ((128, 256), (64, 256), (256, 256)):
+        for base in range(0, rows, 16):
+            for kk in range(rb // 64):
+                addrs = [lib.lsm_frag16_kc_offset(l, base, kk, rb) for l in range(64)]
+                assert degree(addrs, 16) == 1
 
 
-def test_16x16_transposed_reads_are_two_way(layouts):
-    # ds_read_b64_tr_b16 on a 512-byte-row B tile: a 32-lane phase reads
-    # k-rows {k..k+3} and {k+8..k+11}, whose chunks the period-4 swizzle puts
-    # in the same banks, so these reads are 2-way (the 32 x 32 ones are not)
+def test_16x16_k_contig_offset_is_base_rows_plus_lane_part(layouts):
+    # frag16_kc_offset splits into base * row_bytes and the lane's part, which
+    # relies on every K-contiguous swizzle having a period dividing 16 rows
     lib = layouts["swizzled"]
+    for rb in (64, 128, 256):
+        for base in range(0, 256, 16):
+            for kk in range(rb // 64):
+                for l in range(64):
+                    row, chunk = base + (l & 15), 4 * kk + (l >> 4)
+                    assert lib.lsm_frag16_kc_offset(l, base, kk, rb) == \
+                        lib.lsm_kc_chunk_offset(row, chunk, rb)
+
+
+def tr16_read_degree(off, row_bytes):
     worst = 1
-    for base in range(0, 256, 16):
+    for base in range(0, row_bytes // 2, 16):
         for kk in range(2):
             for h in range(2):
-                addrs = [lib.lsm_frag16_tr_offset(l, base, kk, h, 512) for l in range(64)]
-                worst = max(worst, degree(addrs, 8))
-    assert worst == 2
+                worst = max(worst, degree([off(l, base, kk, h, row_bytes) for l in range(64)], 8))
+    return worst
+
+
+@pytest.mark.parametrize("row_bytes", [512, 256])
+def test_16x16_transposed_reads_are_conflict_free(layouts, row_bytes):
+    # ds_read_b64_tr_b16 on a tile with 256- or 512-byte rows: a 32-lane
+    # phase reads k-rows {k..k+3} and {k+8..k+11}, 32 bytes each; the
+    # 16 x 16 x 32 swizzle puts the eight rows in the eight 32-byte eighths of
+    # the bank line
+    assert tr16_read_degree(layouts["swizzled"].lsm_frag16_tr_offset, row_bytes) == 1
+
+
+def test_16x16_transposed_reads_need_their_own_swizzle(layouts):
+    # the same reads on the 32 x 32 fragments' layout (period 4 in k) put
+    # rows k and k+8 on the same banks: 2-way; unswizzled, 8-way
+    lib = layouts["swizzled"]
+
+    def on_mn32_layout(l, base, kk, h, rb):
+        k = 32 * kk + 8 * (l >> 4) + 4 * h + ((l >> 2) & 3)
+        return lib.lsm_mn_chunk_offset(k, (base + 4 * (l & 3)) // 8, rb) + 8 * (l & 1)
+    assert tr16_read_degree(on_mn32_layout, 512) == 2
+    assert tr16_read_degree(layouts["linear"].lsm_frag16_tr_offset, 512) == 8
+
+
+@pytest.mark.parametrize("row_bytes", [512, 256])
+def test_16x16_transposed_offset_matches_its_definition(layouts, row_bytes):
+    # frag16_tr_offset is written as lane part XOR fragment bits (what the
+    # kernel evaluates); it must equal the plain definition: k-row
+    # 32 kk + 8 (l >> 4) + 4 h + ((l >> 2) & 3), chunk (base + 4 (l & 3)) / 8 of
+    # the 16 x 16 x 32 layout, byte 8 (l & 1) of the chunk
+    for name, lib in layouts.items():
+        for base in range(0, row_bytes // 2, 16):
+            for kk in range(2):
+                for h in range(2):
+                    for l in range(64):
+                        k = 32 * kk + 8 * (l >> 4) + 4 * h + ((l >> 2) & 3)
+                        want = lib.lsm_mn16_chunk_offset(k, (base + 4 * (l & 3)) // 8, row_bytes) \
+                            + 8 * (l & 1)
+                        assert lib.lsm_frag16_tr_offset(l, base, kk, h, row_bytes) == want, name
+
+
+@pytest.mark.parametrize("row_bytes", [512, 256])
+def test_16x16_swizzle_repeats_every_second_load_round(layouts, row_bytes):
+    # The ping-pong kernel's loader (256 threads) moves 4096 / row_bytes k-rows
+    # per round and keeps two lane offsets, one for even and one for odd
+    # rounds; that is right only if the swizzle of row r + d * step equals
+    # the swizzle of row r + (d mod 2) * step for every round d.
+    lib = layouts["swizzled"]
+    step = 4096 // row_bytes
+    for r in range(step):
+        for d in range(64 // step):
+            assert lib.lsm_mn16_swizzle(r + d * step, row_bytes) == \
+                lib.lsm_mn16_swizzle(r + (d % 2) * step, row_bytes)
+    # 512-byte rows (8-row rounds): a one-offset loader would be wrong, the
+    # period is two rounds; 256-byte rows (16-row rounds): one offset serves
+    differs = any(lib.lsm_mn16_swizzle(r + step, row_bytes) != lib.lsm_mn16_swizzle(r, row_bytes)
+                  for r in range(step))
+    assert differs == (step % 16 != 0)
+
+
+def tr16_redistribute(src):
+    """ds_read_b64_tr_b16 lane exchange on gfx950 (pinned on the GPU by the
+    hardware-map probe tests): inside each aligned group of 16 lanes,
+    destination lane d receives as element j the element d & 3 of source
+    lane (d >> 2) + 4 j.  `src` is the 64 lanes' 4-element vectors."""
+    out = []
+    for d in range(64):
+        g = d & ~15
+        out.append([src[g + ((d & 15) >> 2) + 4 * j][d & 3] for j in range(4)])
+    return out
+
+
+@pytest.mark.parametrize("row_bytes", [512, 256])
+def test_16x16_lds_image_gives_each_lane_its_mfma_operand(layouts, row_bytes):
+    # Build the LDS image the loader writes (loader_lds_offset16: logical
+    # chunk c of k-row r at its swizzled place), read every fragment with
+    # frag16_tr_offset and the lane exchange, and check that lane l ends with
+    # column base + (l & 15), k = 32 kk + 8 (l >> 4) + 0..7 -- the operand
+    # layout of v_mfma_f32_16x16x32.
+    lib = layouts["swizzled"]
+    width, krows = row_bytes // 2, 64
+    image = {}
+    for cid in range(krows * row_bytes // 16):
+        r, c = cid // (row_bytes // 16), cid % (row_bytes // 16)
+        phys = lib.lsm_loader_lds_offset16(cid, row_bytes)
+        assert phys == lib.lsm_mn16_chunk_offset(r, c, row_bytes)
+        for e in range(8):
+            image[phys + 2 * e] = (r, 8 * c + e)
+    assert len(image) == krows * width
+    for base in range(0, width, 16):
+        for kk in range(2):
+            frag = [[] for _ in range(64)]
+            for h in range(2):
+                src = [[image[lib.lsm_frag16_tr_offset(l, base, kk, h, row_bytes) + 2 * e]
+                        for e in range(4)] for l in range(64)]
+                for l, v in enumerate(tr16_redistribute(src)):
+                    frag[l] += v
+            for l in range(64):
+                assert frag[l] == [(32 * kk + 8 * (l >> 4) + i, base + (l & 15)) for i in range(8)]
 
 
 # ------------------------------------------------------------------ epilogue staging
