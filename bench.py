@@ -55,7 +55,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, KERNEL_DIR)
     for name in sorted(os.listdir(d)):
-        if name.endswith((".h", ".hip")):
+        # the GEMM sources; hw_probe.hip holds test probes, not GEMM kernels
+        if name.endswith((".h", ".hip")) and name != "hw_probe.hip":
             h.update(name.encode())
             with open(os.path.join(d, name), encoding="utf-8") as f:
                 h.update(_code_only(f.read()).encode())
@@ -127,6 +128,54 @@ def cpu_baseline(p, rows):
                       f"{p.M}x{p.N}x{p.K} problem ({rows * p.N} outputs), {dt:.2f} s wall"}
 
 
+def lds_pad_probe(iters=4096, launches=50, repeats=9):
+    """The padding table's measurement ("Lds Optimization", "Optimization
+    Method 2: Padding", measured table): one wave reads a strided column of a
+    64 x (64 + PAD) fp16 LDS tile, `iters` dependent reads per launch; per PAD
+    the best of `repeats` runs of `launches` launches (HIP events on the
+    launch stream).  Prints one JSON line: ms per run and the conflict degree
+    the bank model predicts (64 banks of 4 bytes, a whole wave per 2-byte
+    access)."""
+    import ctypes
+    import torch
+    from lds_staged_matrix_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.HW_PROBE)
+    lib.lsm_probe_pad.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lsm_probe_pad.restype = ctypes.c_int
+    out = torch.zeros(1, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for pad in (0, 1, 2, 4, 32):
+        def launch():
+            if lib.lsm_probe_pad(pad, iters, out.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("lsm_probe_pad failed")
+        for _ in range(5):
+            launch()
+        best = None
+        for _ in range(repeats):
+            s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(launches):
+                launch()
+            e0.record(stream)
+            torch.cuda.synchronize()
+            ms = s0.elapsed_time(e0)
+            best = ms if best is None else min(best, ms)
+        stride_dw = (64 + pad) * 2 / 4.0
+        banks = {}
+        for t in range(64):
+            dw = int((t * (64 + pad) * 2) // 4)
+            banks.setdefault(dw % 64, set()).add(dw)
+        res[f"pad{pad}"] = {"best_ms_per_run": round(best, 4), "launches_per_run": launches,
+                            "reads_per_launch": iters, "row_bytes": 2 * (64 + pad),
+                            "model_way": max(len(v) for v in banks.values()),
+                            "row_stride_dwords": stride_dw}
+        log(f"pad {pad}: best {best:.4f} ms per {launches} launches")
+    assert float(out.item()) == 0.0
+    print(json.dumps({"probe": "lds padded column read, one wave, 64 x (64 + PAD) fp16",
+                      "results": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +204,10 @@ def main():
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
+    ap.add_argument("--lds-pad-probe", action="store_true",
+                    help="time the one-wave strided column read of a 64 x (64 + PAD) fp16 LDS "
+                         "tile for PAD 0, 1, 2, 4, 32 (the padding table's probe), for "
+                         "calibrating the bank-conflict counters under rocprofv3 --pmc")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
@@ -179,6 +232,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read, {n} bytes written")
+        return
+
+    if args.lds_pad_probe:
+        lds_pad_probe()
         return
 
     w = dict(synth.WORKLOADS[args.workload])

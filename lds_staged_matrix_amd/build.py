@@ -5,7 +5,10 @@ Also builds, from the same sources:
     design choice (see VARIANTS), used by the benchmark and the counter runs
     that measure what each choice buys;
   * liblds_layout_host.so (and _noswizzle) -- host-only builds of the LDS
-    address functions, evaluated by the bank-conflict model in the tests.
+    address functions, evaluated by the bank-conflict model in the tests;
+  * libhw_probe.so -- one-wave probe kernels of the hardware behaviour the
+    kernels rely on (fragment reads, MFMA layouts, buffer range checks, padded
+    LDS column reads), for the tests and the benchmark's probe mode.
 """
 import os
 import subprocess
@@ -31,9 +34,11 @@ VARIANTS = {
     "stage1": ["-DLSM_DMA_STAGES=1"],       # 128/64 direct-to-LDS kernel with one LDS stage, no overlap
     "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
     "mfma32": ["-DLSM_PP_MFMA=32"],         # 16-bit ping-pong kernel on 32x32x16 instead of 16x16x32 MFMAs
+    "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}
+HW_PROBE = os.path.join(PKG, "libhw_probe.so")
 
 
 def variant_path(name: str) -> str:
@@ -71,6 +76,12 @@ def build(verbose: bool = False, extra_flags=(), variant: str = None) -> str:
     return _run(cmd, out, verbose)
 
 
+def build_hw_probe(verbose: bool = False) -> str:
+    """The probe kernels (device code, same flags as the library)."""
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "hw_probe.hip"), "-o", HW_PROBE + ".tmp"]
+    return _run(cmd, HW_PROBE, verbose)
+
+
 def build_layout_host(verbose: bool = False):
     """Host-only builds of the LDS address functions (no device code)."""
     outs = []
@@ -86,7 +97,7 @@ def build_all(verbose: bool = False):
     """Every build, six hipcc processes at a time."""
     from concurrent.futures import ThreadPoolExecutor
     jobs = [lambda: build(verbose)] + [lambda n=n: build(verbose, variant=n) for n in VARIANTS] + \
-           [lambda: build_layout_host(verbose)]
+           [lambda: build_layout_host(verbose), lambda: build_hw_probe(verbose)]
     with ThreadPoolExecutor(max_workers=6) as pool:
         for f in [pool.submit(j) for j in jobs]:
             f.result()

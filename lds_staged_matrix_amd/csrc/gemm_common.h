@@ -15,6 +15,19 @@
 #define LSM_TR_READ 1
 #endif
 
+// LSM_LDS_POISON = 1 builds the kernels so that they fill their LDS with NaN
+// bits (all-ones bytes: NaN as bf16, fp16 and E4M3) before its first use, and
+// fill the epilogue's staging region and the split-K reduction region the
+// same way before those are written.  A read of a slot that no load or write
+// has filled then turns the products it reaches into NaN, which a bit-exact
+// comparison on integer inputs reports ("Lds Optimization", "LDS Instruction
+// Model" and "Verification Checklist": every read must follow the write it
+// needs).  It exists only for the A/B build that checks this; the library is
+// built with 0.
+#ifndef LSM_LDS_POISON
+#define LSM_LDS_POISON 0
+#endif
+
 namespace lsm {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -101,6 +114,15 @@ struct OperandTile {
                    : mf16 ? mn16_swizzle(row, ROW_BYTES) : mn_swizzle(row, ROW_BYTES, ES);
   }
 };
+
+// Poison build: `n` threads (thread index `t`) fill `bytes` bytes of LDS at
+// `lds` (16-byte aligned, a multiple of 16) with all-ones bytes.  No-op in the
+// library.  The caller orders it before the region's first use.
+__device__ __forceinline__ void lds_poison(char *lds, int bytes, int t, int n) {
+  if constexpr (LSM_LDS_POISON) {
+    for (int i = t; i < bytes / 16; i += n) ((u32x4 *)lds)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+  }
+}
 
 template <int IN>
 __device__ __forceinline__ v16f32 mfma_32x32x16(v8i16 a, v8i16 b, v16f32 c) {
@@ -337,6 +359,7 @@ __device__ __forceinline__ void epilogue_lds(void *C,
   constexpr int RPI = 64 * 16 / ROWB;                        // rows per 64-lane read
   char *mine = lds + wave * PR * ROWB;
   auto off = [&](int row, int chunk) { return epi_stage_offset(row, chunk, ROWB, MF); };
+  lds_poison(mine, PR * ROWB, lane, 64);   // poison build: the wave's region, before its writes
   const int grow0 = m0 + wm * T::TM;
   const int gcol0 = n0 + wn * T::TN;
 #pragma unroll

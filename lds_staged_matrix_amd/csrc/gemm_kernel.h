@@ -82,6 +82,10 @@ __global__ __launch_bounds__(T::NT) void lds_gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  if constexpr (LSM_LDS_POISON) {   // poison build: all of LDS, before any load or write
+    lds_poison(smem, 2 * STAGE, tid, blockDim.x);
+    __syncthreads();
+  }
   const int wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
 

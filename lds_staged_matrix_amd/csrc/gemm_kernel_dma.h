@@ -206,6 +206,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  if constexpr (LSM_LDS_POISON) {   // poison build: all of LDS, before any load or write
+    lds_poison(smem, STAGES * STAGE, tid, blockDim.x);
+    __syncthreads();
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
 

@@ -90,6 +90,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  if constexpr (LSM_LDS_POISON) {   // poison build: all of LDS, before any load or write
+    lds_poison(smem, 2 * STAGE, tid, blockDim.x);
+    __syncthreads();
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int group = wave >> 2;                           // 0: waves 0-3, 1: waves 4-7
   const int wm = group, wn = wave & 3;

@@ -64,6 +64,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_skinny_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  if constexpr (LSM_LDS_POISON) {   // poison build: all of LDS, before any load or write
+    lds_poison(smem, T::NS * STAGE, tid, blockDim.x);
+    __syncthreads();
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   tile_coords(xcd_logical_id(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, T::GROUP_M, tm, tn);
@@ -145,6 +149,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_skinny_kernel(
 
   // Sum the four waves' partial tiles through LDS, in wave order.
   __syncthreads();                                       // every wave is done with the ring
+  if constexpr (LSM_LDS_POISON) {   // poison build: the reduction region, before its writes
+    lds_poison(smem, RED, tid, T::NT);
+    __syncthreads();
+  }
   // Slot of accumulator register r of block (i, j) of wave w, lane l.
   auto red_at = [&](int w, int i, int j, int r) { return (((w * T::FM + i) * T::FN + j) * 16 + r) * 64 + lane; };
   float *red = (float *)smem;

@@ -36,6 +36,9 @@ int lsm_frag16_tr_lane(int lane, int row_bytes) { return lsm::frag16_tr_lane(lan
 int lsm_epi_stage_offset(int row, int chunk, int row_bytes, int mf) {
   return lsm::epi_stage_offset(row, chunk, row_bytes, mf);
 }
+int lsm_mn_chunk_offset8(int k, int chunk, int row_bytes) {
+  return lsm::mn_chunk_offset(k, chunk, row_bytes, 1);
+}
 int lsm_loader_lds_offset8(int id, int row_bytes, int k_contig) {
   return lsm::loader_lds_offset(id, row_bytes, k_contig != 0, 1);
 }

@@ -102,6 +102,42 @@ def oracle_entries(p, rows, cols):
                                OLAYOUT[p.layoutB], ODTYPE[p.dtype], rows, cols)
 
 
+def _pool_map(fn, items):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(16, oracle.max_threads()))) as pool:
+        return list(pool.map(fn, items))
+
+
+def oracle_row_set(p, rows):
+    """Full rows `rows` of C (len(rows) x N), one single-threaded oracle call
+    per row, the calls spread over the host's cores."""
+    return np.stack(_pool_map(lambda r: oracle.gemm_rows(
+        p.A, p.B, p.M, p.N, p.K, p.lda, p.ldb, OLAYOUT[p.layoutA], OLAYOUT[p.layoutB],
+        ODTYPE[p.dtype], int(r), int(r) + 1, threads=1)[0], rows))
+
+
+def oracle_col_set(p, cols):
+    """Full columns `cols` of C (len(cols) x M), as rows of the transposed
+    product C^T = B^T A^T: the same bytes read as B^T (A^T) with the layout
+    flag B (A) had, which the oracle's transpose pin checks."""
+    return np.stack(_pool_map(lambda c: oracle.gemm_rows(
+        p.B, p.A, p.N, p.M, p.K, p.ldb, p.lda, OLAYOUT[p.layoutB], OLAYOUT[p.layoutA],
+        ODTYPE[p.dtype], int(c), int(c) + 1, threads=1)[0], cols))
+
+
+def every_tile_rows_cols(M, N, tile=256, seed=0):
+    """One row inside every tile row and one column inside every tile column
+    of a tile x tile grid, at varying positions within the tile (including
+    the tile's first and last), so that every tile has a checked full row and
+    a checked full column."""
+    rng = np.random.default_rng(seed)
+    rows = [min(M - 1, t + (0 if i == 0 else tile - 1 if i == 1 else int(rng.integers(0, tile))))
+            for i, t in enumerate(range(0, M, tile))]
+    cols = [min(N - 1, t + (tile - 1 if i == 0 else 0 if i == 1 else int(rng.integers(0, tile))))
+            for i, t in enumerate(range(0, N, tile))]
+    return rows, cols
+
+
 def gpu_values(C, gdtype):
     """Decoded fp64 values of a GPU output block (numpy)."""
     out = OUT_OF[gdtype]

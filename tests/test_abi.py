@@ -143,3 +143,16 @@ def test_binding_refuses_integers_the_abi_cannot_hold(lib, pos, value):
         lsm.gemm_run(FAKE, *args)
     with pytest.raises(OverflowError):
         lsm.gemm_status_str(1 << 32)
+
+
+def test_probe_library_loads_and_exports_its_probes():
+    # libhw_probe.so (test infrastructure: the hardware-map probes) loads
+    # without a GPU and exports every probe the GPU tests call
+    from lds_staged_matrix_amd import build as hip_build
+    import ctypes
+    assert os.path.exists(hip_build.HW_PROBE), "build libhw_probe.so first"
+    ctypes.CDLL(hip_build.HW_PROBE)
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.HW_PROBE], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert {"lsm_probe_frag", "lsm_probe_mfma", "lsm_probe_range", "lsm_probe_pad"} <= exported

@@ -79,12 +79,13 @@ CASES8 = [
 ]
 
 
-def check(cls, M, N, K, la, lb, gd, seed, dist):
+def check(cls, M, N, K, la, lb, gd, seed, dist, lib=None, what="every-kernel"):
+    """One case against the oracle; `lib` = (Library, handle) runs an A/B build."""
     es = 1 if H.IN_OF[gd] == synth.E4M3 else 2
     assert shape_class(M, N, K, la, lb, es) == cls, (cls, M, N, K, la, lb)
-    print(f"CASE every-kernel {cls} {M}x{N}x{K} {la}{lb} dtype {gd} {dist}", flush=True)
+    print(f"CASE {what} {cls} {M}x{N}x{K} {la}{lb} dtype {gd} {dist}", flush=True)
     p = H.problem(M, N, K, H.IN_OF[gd], la, lb, dist, (seed, seed + 1))
-    C = H.run_gpu(p, gd, extra_rows=1)
+    C = H.run_gpu(p, gd, extra_rows=1, lib=lib)
     H.assert_canary(C, M, N, gd)
     rows = sorted({0, 1, min(M - 1, 63), min(M - 1, 64), M // 2, M - 2, M - 1})
     want = H.oracle_entries(p, np.repeat(rows, N), np.tile(np.arange(N), len(rows)))

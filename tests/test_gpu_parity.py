@@ -223,20 +223,40 @@ def sample_check(p, C, gdtype, exact, rows_sel, n_entries=4000, seed=0):
         H.assert_close(C[rows, cols], ref, p.K, gdtype, "entries")
 
 
+def every_tile_check(p, C, gdtype, exact, seed=0):
+    """A full row in every 256-row tile row and a full column in every
+    256-column tile column of C against the oracle: every 256 x 256 tile of
+    the launch has a checked row and a checked column."""
+    rows, cols = H.every_tile_rows_cols(p.M, p.N, 256, seed)
+    ref_r = H.oracle_row_set(p, rows)
+    ref_c = H.oracle_col_set(p, cols)
+    got_r = C[rows, :p.N]
+    got_c = np.ascontiguousarray(C[:p.M, cols].T)
+    if exact:
+        H.assert_exact(got_r, ref_r, gdtype, "tile rows")
+        H.assert_exact(got_c, ref_c, gdtype, "tile columns")
+    else:
+        H.assert_close(got_r, ref_r, p.K, gdtype, "tile rows")
+        H.assert_close(got_c, ref_c, p.K, gdtype, "tile columns")
+
+
 @pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
 def test_config_4096_all_layouts_bf16_out(la, lb):
     w = synth.WORKLOADS["bf16_4096_all_bf16"]
     announce(4096, la, lb)
     p = H.problem(4096, 4096, 4096, synth.BF16, la, lb, w["dist"], w["seeds"])
     C = H.run_gpu(p, lsm.GEMM_BF16_BF16)
-    sample_check(p, C, lsm.GEMM_BF16_BF16, False, [(0, 2), (4094, 4096)], 3000)
+    every_tile_check(p, C, lsm.GEMM_BF16_BF16, False, seed=3)
+    sample_check(p, C, lsm.GEMM_BF16_BF16, False, [], 3000)
 
 
-def test_config_4096_integer_exact():
-    announce(4096, "int")
-    p = H.problem(4096, 4096, 4096, synth.BF16, "K", "MN", "int", (3001, 3002))
+@pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
+def test_config_4096_integer_exact(la, lb):
+    announce(4096, "int", la, lb)
+    p = H.problem(4096, 4096, 4096, synth.BF16, la, lb, "int", (3001, 3002))
     C = H.run_gpu(p, lsm.GEMM_BF16_BF16)
-    sample_check(p, C, lsm.GEMM_BF16_BF16, True, [(0, 2), (2047, 2049), (4095, 4096)], 3000)
+    every_tile_check(p, C, lsm.GEMM_BF16_BF16, True, seed=4)
+    sample_check(p, C, lsm.GEMM_BF16_BF16, True, [], 3000)
 
 
 def test_config_8192_nn_f32():
@@ -244,14 +264,16 @@ def test_config_8192_nn_f32():
     announce(8192, "normal")
     p = H.problem(8192, 8192, 8192, synth.BF16, "K", "MN", w["dist"], w["seeds"])
     C = H.run_gpu(p, lsm.GEMM_BF16_F32)
-    sample_check(p, C, lsm.GEMM_BF16_F32, False, [(0, 2), (8191, 8192)], 2000)
+    every_tile_check(p, C, lsm.GEMM_BF16_F32, False, seed=5)
+    sample_check(p, C, lsm.GEMM_BF16_F32, False, [], 2000)
 
 
 def test_config_8192_integer_exact():
     announce(8192, "int")
     p = H.problem(8192, 8192, 8192, synth.BF16, "K", "MN", "int", (4001, 4002))
     C = H.run_gpu(p, lsm.GEMM_BF16_F32)
-    sample_check(p, C, lsm.GEMM_BF16_F32, True, [(0, 1), (4100, 4101), (8191, 8192)], 2000)
+    every_tile_check(p, C, lsm.GEMM_BF16_F32, True, seed=6)
+    sample_check(p, C, lsm.GEMM_BF16_F32, True, [], 2000)
 
 
 # M <= 32 with whole 16-byte chunks along every contiguous extent: the
