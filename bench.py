@@ -128,6 +128,46 @@ def cpu_baseline(p, rows):
                       f"{p.M}x{p.N}x{p.K} problem ({rows * p.N} outputs), {dt:.2f} s wall"}
 
 
+def cpu_baseline_all(flop_budget=1.0e10):
+    """The oracle, as it stands, timed on this host's cores for every
+    workload: configurations small enough for it (256^3, 1500x1152x896) in
+    full, one untimed and one timed run, on all cores and on one core; the
+    others on their first rows, about `flop_budget` flops' worth, every
+    layout.  Prints one JSON line; nothing here touches the GPU."""
+    import oracle
+    ol = {"K": oracle.K_CONTIG, "MN": oracle.MN_CONTIG}
+    od = {synth.BF16: oracle.BF16, synth.F16: oracle.F16, synth.E4M3: oracle.E4M3}
+    cores = oracle.max_threads()
+    out = {}
+    for name, w in synth.WORKLOADS.items():
+        full = 2.0 * w["M"] * w["N"] * w["K"] <= 4e9     # 256^3 and 1500x1152x896
+        for la, lb in w["layouts"]:
+            p = synth.make_problem(w["M"], w["N"], w["K"], w["dtype"], la, lb, w["dist"],
+                                   w["seeds"][0], w["seeds"][1], w["scale"])
+            rows = p.M if full else max(1, min(p.M, int(flop_budget / (2.0 * p.N * p.K))))
+
+            def run(threads):
+                t0 = time.perf_counter()
+                oracle.gemm_rows(p.A, p.B, p.M, p.N, p.K, p.lda, p.ldb, ol[la], ol[lb],
+                                 od[p.dtype], 0, rows, threads=threads)
+                return time.perf_counter() - t0
+            rec = {"rows": rows, "of_rows": p.M, "cores": cores}
+            if full:
+                run(0)                                   # untimed
+            dt = run(0)
+            flops = 2.0 * rows * p.N * p.K
+            rec.update(seconds=round(dt, 4), gflops=round(flops / dt / 1e9, 3))
+            if full:
+                dt1 = run(1)
+                rec.update(single_core_seconds=round(dt1, 4),
+                           single_core_gflops=round(flops / dt1 / 1e9, 3))
+            key = name if len(w["layouts"]) == 1 else f"{name} {la},{lb}"
+            out[key] = rec
+            log(f"cpu baseline {key}: {rec}")
+    print(json.dumps({"cpu_baseline": "oracle fp64 m->k->n loop (OpenMP over m)", "cores": cores,
+                      "results": out}), flush=True)
+
+
 def lds_pad_probe(iters=4096, launches=50, repeats=9):
     """The padding table's measurement ("Lds Optimization", "Optimization
     Method 2: Padding", measured table): one wave reads a strided column of a
@@ -208,6 +248,8 @@ def main():
                     help="time the one-wave strided column read of a 64 x (64 + PAD) fp16 LDS "
                          "tile for PAD 0, 1, 2, 4, 32 (the padding table's probe), for "
                          "calibrating the bank-conflict counters under rocprofv3 --pmc")
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="time the oracle on this host for every workload (no GPU use) and exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
@@ -218,6 +260,10 @@ def main():
         print("bench.py measures one GPU only: this is a single-GPU kernel library "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_baseline_all:
+        cpu_baseline_all()
+        return
 
     import torch
     import lds_staged_matrix_amd as lsm

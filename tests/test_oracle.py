@@ -114,6 +114,35 @@ def test_encode_bf16_vs_bit_trick_sampled_fp32(oracle_lib):
     assert bad.size == 0, f"{bad.size} mismatches, first {u[bad[:5]]}"
 
 
+def test_encode_bf16_vs_bit_trick_every_fp32_pattern(oracle_lib):
+    # Every one of the 2^32 fp32 bit patterns, widened exactly to fp64 and
+    # rounded by the oracle, against the bit-trick formula on the fp32 bits:
+    # finite values and infinities bit for bit; every NaN pattern must give
+    # the canonical quiet NaN (where the bit trick would carry a NaN with a
+    # small payload into the exponent and produce infinity).  Chunks of 2^24
+    # patterns run on a thread pool (the oracle call and numpy release the
+    # interpreter lock).
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 24
+
+    def check(c):
+        u = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32)
+        got = oracle.encode(u.view(np.float32).astype(np.float64), oracle.BF16)
+        nan = (u & 0x7F800000) == 0x7F800000
+        nan &= (u & 0x007FFFFF) != 0
+        want = _bf16_bit_trick(u)
+        bad = np.count_nonzero((got != want) & ~nan)
+        bad_nan = np.count_nonzero(got[nan] != 0x7FC0)
+        return bad, bad_nan, int(np.count_nonzero(nan))
+
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        res = list(pool.map(check, range((1 << 32) // chunk)))
+    assert sum(r[0] for r in res) == 0, "finite/infinite patterns differ from the bit trick"
+    assert sum(r[1] for r in res) == 0, "a NaN pattern did not give the canonical NaN"
+    assert sum(r[2] for r in res) == 2 * ((1 << 23) - 1), "NaN pattern count"
+
+
 def test_encode_f16_vs_numpy_sampled(oracle_lib):
     rng = np.random.default_rng(777)
     # wide-range random doubles, including the subnormal and overflow ranges
