@@ -160,9 +160,10 @@ __device__ __forceinline__ v4f32 mfma_16x16x32(v8i16 a, v8i16 b, v4f32 c) {
 }
 
 // Accumulator layouts of the two MFMA shapes.  Register r of lane l holds
-//   32 x 32 block (16 registers): row 8*(r >> 2) + 4*(l >> 5) + (r & 3), column l & 31
-//     (checked with a probe);
+//   32 x 32 block (16 registers): row 8*(r >> 2) + 4*(l >> 5) + (r & 3), column l & 31;
 //   16 x 16 block (4 registers):  row 4*(l >> 4) + r, column l & 15.
+// Both are checked on the GPU, one MFMA at a time on random and one-hot
+// integers, by the probe kernels of hw_probe.hip (tests/test_gpu_hw_maps.py).
 // row() is the whole row; lane_row() + reg_row() splits it into its lane and register parts.
 template <int MF>
 struct AccLayout;

@@ -33,8 +33,10 @@
 //    Dive into LDS Optimizations on AMD Instinct MI450 GPUs", Part I, end of
 //    "What Does ds_load_tr Do?").
 //
-// Lane redistribution of ds_read_b64_tr_b16 on gfx950, measured with a probe
-// kernel: inside each aligned group of 16 lanes, destination lane d receives,
+// Lane redistribution of ds_read_b64_tr_b16 on gfx950 (measured on MI355X;
+// tests/test_gpu_hw_maps.py reads every fragment of every tile kind through
+// the probe kernels of hw_probe.hip and checks it against these functions):
+// inside each aligned group of 16 lanes, destination lane d receives,
 // as its element j (j = 0..3), element (d & 3) of source lane (d >> 2) + 4*j.
 // Hence, for destination lane d to hold column c0 + d of rows r0..r0+3,
 // source lane s reads row r0 + (s >> 2), columns c0 + 4*(s & 3) .. +3.
@@ -125,7 +127,8 @@ __host__ __device__ constexpr int loader_lds_offset16(int id, int row_bytes) {
 
 // ---------------------------------------------------------------- fragment reads
 //
-// Fragments of v_mfma_f32_32x32x16_{bf16,f16} (layout checked with a probe):
+// Fragments of v_mfma_f32_32x32x16_{bf16,f16} (checked on the GPU by the
+// hardware-map probes, tests/test_gpu_hw_maps.py):
 // lane l holds operand row/column (l & 31) and k = 8*(l >> 5) + i, i = 0..7,
 // for both A and B.  `base` is the first M/N index of the 32-wide fragment
 // inside the tile, `kk` the 16-deep k step inside the tile.
@@ -184,7 +187,7 @@ __host__ __device__ constexpr int frag16_tr_offset(int lane, int base, int kk, i
 }
 
 // Fragments of v_mfma_scale_f32_32x32x64_f8f6f4 on 8-bit elements (checked
-// with a probe): lane l holds operand row/column (l & 31) and 32 bytes; the
+// on the GPU by the hardware-map probes): lane l holds operand row/column (l & 31) and 32 bytes; the
 // k of byte b only has to be the same for A and B, and here it is
 // k = 64*kk + 32*(l >> 5) + b.
 
@@ -195,8 +198,8 @@ __host__ __device__ constexpr int frag_kc8_offset(int lane, int base, int kk, in
 }
 
 // MN-contiguous 8-bit operand: four ds_read_b64_tr_b8 per fragment, q = 0..3
-// delivering bytes 8q .. 8q + 7.  ds_read_b64_tr_b8 on gfx950 (measured with
-// a probe): inside each aligned group of 16 lanes, destination lane d
+// delivering bytes 8q .. 8q + 7.  ds_read_b64_tr_b8 on gfx950 (measured, and
+// checked on the GPU by the hardware-map probes): inside each aligned group of 16 lanes, destination lane d
 // receives as byte j the byte (d & 7) of source lane (d >> 3) + 2j.  So
 // source lane s of group g (s' = s & 15) reads k-row
 // 64*kk + 32*(g >> 1) + 8q + (s' >> 1) at columns base + 16*(g & 1) +
