@@ -33,7 +33,7 @@ VARIANTS = {
     "noxcd": ["-DLSM_XCD_REMAP=0"],         # tiles in hardware workgroup order, not grouped per XCD
     "stage1": ["-DLSM_DMA_STAGES=1"],       # 128/64 direct-to-LDS kernel with one LDS stage, no overlap
     "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
-    "mfma32": ["-DLSM_PP_MFMA=32"],         # 16-bit ping-pong kernel on 32x32x16 instead of 16x16x32 MFMAs
+    "mfma32": ["-DLSM_PP_MFMA=32", "-DLSM_PP_MFMA8=32"],   # ping-pong kernel on 32x32 MFMAs (32x32x16, fp8 32x32x64)
     "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
 }
 

@@ -67,12 +67,16 @@ struct Args {
 // DMA4: the direct-to-LDS kernel with four LDS stages (operand panels beyond the L2).
 enum Kind { REG = 0, DMA = 1, PINGPONG = 2, SKINNY = 3, DMA4 = 4 };
 
-// The ping-pong kernel's 16-bit instances run on v_mfma_f32_16x16x32.
-// LSM_PP_MFMA = 32 builds them with v_mfma_f32_32x32x16 instead; it exists
-// only for the A/B build that measures the MFMA shape.  The library is built
-// with 16.
+// The ping-pong kernel's 16-bit instances run on v_mfma_f32_16x16x32 and its
+// E4M3 instances on v_mfma_scale_f32_16x16x128_f8f6f4.  LSM_PP_MFMA = 32 and
+// LSM_PP_MFMA8 = 32 build them with the 32 x 32 forms instead (32x32x16,
+// 32x32x64); they exist only for the A/B build that measures the MFMA shape.
+// The library is built with 16.
 #ifndef LSM_PP_MFMA
 #define LSM_PP_MFMA 16
+#endif
+#ifndef LSM_PP_MFMA8
+#define LSM_PP_MFMA8 16
 #endif
 
 template <class T, int KIND, int LA, int LB, int IN, int OUT>
@@ -91,7 +95,7 @@ static hipError_t launch_dma(const Args &a, hipStream_t stream) {
   const void *fn;
   if constexpr (KIND == PINGPONG)
     fn = (const void *)lds_gemm_pingpong_kernel<T, LA, LB, IN, OUT,
-                                                IN == IN_E4M3 ? 32 : LSM_PP_MFMA>;
+                                                IN == IN_E4M3 ? LSM_PP_MFMA8 : LSM_PP_MFMA>;
   else if constexpr (KIND == DMA4)
     fn = (const void *)lds_gemm_dma_kernel<T, LA, LB, IN, OUT, 4>;
   else

@@ -80,15 +80,16 @@ struct Tile {
 // MN elements.  "outer" is the strided dimension of the operand in memory,
 // "inner" its unit-stride dimension; ES is the element size in bytes.  The
 // tile is filled in rounds of NT 16-byte chunks: chunk id = thread + round *
-// NT, numbered row-major.  MF16 = 1 lays an MN-contiguous 16-bit tile out for
-// the transposed fragments of the 16 x 16 x 32 MFMA (mn16_chunk_offset);
-// otherwise, and for K-contiguous tiles, the layout is the one the 32 x 32
-// fragments read (kc_chunk_offset, mn_chunk_offset).
+// NT, numbered row-major.  MF16 = 1 lays an MN-contiguous tile out for the
+// transposed fragments of the 16 x 16 MFMAs (mn16_chunk_offset: 16 x 16 x 32
+// for 16-bit, 16 x 16 x 128 for 8-bit elements); otherwise, and for
+// K-contiguous tiles, the layout is the one the 32 x 32 fragments read
+// (kc_chunk_offset, mn_chunk_offset).
 template <int MN, int BK, int LAYOUT, int NT, int ES_ = 2, int MF16_ = 0>
 struct OperandTile {
   static constexpr bool kcontig = LAYOUT == KC;
   static constexpr int ES = ES_;
-  static constexpr bool mf16 = MF16_ != 0 && !kcontig;          // 16 x 16 x 32 MN layout
+  static constexpr bool mf16 = MF16_ != 0 && !kcontig;          // 16 x 16 MN layout
   static constexpr int ROWS = kcontig ? MN : BK;                 // outer extent
   static constexpr int INNER = kcontig ? BK : MN;                // inner extent (elements)
   static constexpr int ROW_BYTES = ES * INNER;
@@ -98,20 +99,29 @@ struct OperandTile {
   static constexpr int CHUNKS = BYTES / 16;
   static constexpr int LOADS = CHUNKS / NT;                      // 16-byte loads per thread
   static constexpr int ROW_STEP = NT / CPR;                      // rows between a thread's loads
-  static constexpr int SWZ_PERIOD = kcontig ? 16 : mf16 ? 16 : (ES == 2 ? 4 : 8);   // rows per swizzle period
+  // rows per swizzle period
+  static constexpr int SWZ_PERIOD = kcontig ? 16 : mf16 ? (ES == 2 ? 16 : 64) : (ES == 2 ? 4 : 8);
   // A thread's chunks of every load round share one swizzle phase when the
-  // round step is a multiple of the period (one lane offset for all rounds);
-  // the 16 x 16 x 32 MN layout with 8-row rounds alternates two phases (one
-  // lane offset for even and one for odd rounds).
+  // round step is a multiple of the period (one lane offset for all rounds).
+  // The 16 x 16 MN layouts depend on the row only through the row inside a
+  // round and one more bit, that of PHASE_ROWS (8 for 16-bit elements, rounds
+  // of 8 rows; 32 for 8-bit elements, rounds of 16 rows): one lane offset for
+  // the rounds with that bit clear and one for those with it set.
+  static constexpr int PHASE_ROWS = SWZ_PERIOD / 2;
   static constexpr int LANE_OFFSETS = ROW_STEP % SWZ_PERIOD == 0 ? 1 : 2;
-  static_assert(!mf16 || ES == 2, "the 16 x 16 x 32 layout is for 16-bit elements");
   static_assert(CHUNKS % NT == 0, "tile must split evenly into 16-byte loads");
-  static_assert(NT % CPR == 0 && (ROW_STEP % SWZ_PERIOD == 0 || 2 * ROW_STEP == SWZ_PERIOD),
+  static_assert(NT % CPR == 0 && (ROW_STEP % SWZ_PERIOD == 0 ||
+                                  (mf16 && ROW_STEP >= (ES == 2 ? 8 : 16) && PHASE_ROWS % ROW_STEP == 0)),
                 "a thread's chunks must take one or two swizzle phases");
+  // Which of the lane offsets load round d uses.
+  __host__ __device__ static constexpr int round_phase(int d) {
+    return LANE_OFFSETS == 1 ? 0 : ((d * ROW_STEP) / PHASE_ROWS) & 1;
+  }
   // XOR applied to the chunk index of row `row` of this tile.
   __host__ __device__ static constexpr int swizzle(int row) {
     return kcontig ? kc_swizzle(row, ROW_BYTES)
-                   : mf16 ? mn16_swizzle(row, ROW_BYTES) : mn_swizzle(row, ROW_BYTES, ES);
+                   : mf16 ? (ES == 2 ? mn16_swizzle(row, ROW_BYTES) : mn16_swizzle8(row, ROW_BYTES))
+                          : mn_swizzle(row, ROW_BYTES, ES);
   }
 };
 
@@ -145,9 +155,9 @@ __device__ __forceinline__ v16f32 mfma_step(typename InT<IN>::frag a, typename I
     return mfma_32x32x16<IN>(a, b, c);
 }
 
-// One 16 x 16 MFMA step (k = 32) on 16-bit inputs: the 16 x 16 A/B build of
-// the ping-pong kernel ("Lds Optimization", "Optimization Method 3: Increase
-// Write-Read Distance", names v_mfma_f32_16x16x32 as the MFMA it overlaps).
+// One 16 x 16 MFMA step (k = 32) on 16-bit inputs ("Lds Optimization",
+// "Optimization Method 3: Increase Write-Read Distance", names
+// v_mfma_f32_16x16x32 as the MFMA it overlaps).
 template <int IN>
 __device__ __forceinline__ v4f32 mfma_16x16x32(v8i16 a, v8i16 b, v4f32 c) {
   static_assert(IN != IN_E4M3, "16-bit inputs only");
@@ -157,6 +167,22 @@ __device__ __forceinline__ v4f32 mfma_16x16x32(v8i16 a, v8i16 b, v4f32 c) {
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8f16, a),
                                                   __builtin_bit_cast(v8f16, b), c, 0, 0, 0);
+}
+
+// One 16 x 16 MFMA step on E4M3 inputs (k = 128; format code 0 for both
+// operands, E8M0 scales 127 = 2^0, as for the 32 x 32 x 64 form).
+__device__ __forceinline__ v4f32 mfma_16x16x128_e4m3(v8i32 a, v8i32 b, v4f32 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One 16 x 16 MFMA step of the input type.
+template <int IN>
+__device__ __forceinline__ v4f32 mfma16_step(typename InT<IN>::frag a, typename InT<IN>::frag b,
+                                             v4f32 c) {
+  if constexpr (IN == IN_E4M3)
+    return mfma_16x16x128_e4m3(a, b, c);
+  else
+    return mfma_16x16x32<IN>(a, b, c);
 }
 
 // Accumulator layouts of the two MFMA shapes.  Register r of lane l holds
@@ -268,6 +294,62 @@ __device__ __forceinline__ v8i16 read_frag16(const char *lds, int lane, int base
         (lds_v4i16 *)(uintptr_t)(a + 4 * OT::ROW_BYTES));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+}
+
+// One 16 x 128 operand fragment of v_mfma_scale_f32_16x16x128_f8f6f4 on
+// 8-bit elements (k-step kk of 128): lane l gets row/column (l & 15) of the
+// fragment starting at `base`, byte b standing for k = 128*kk + 32*(l >> 4) + b.
+template <class OT>
+__device__ __forceinline__ v8i32 read_frag16_8(const char *lds, int lane, int base, int kk) {
+  static_assert(OT::ES == 1, "8-bit tile");
+  if constexpr (OT::kcontig) {
+    const u32x4 lo = *(const u32x4 *)(lds + frag16_kc8_offset(lane, base, kk, 0, OT::ROW_BYTES));
+    const u32x4 hi = *(const u32x4 *)(lds + frag16_kc8_offset(lane, base, kk, 1, OT::ROW_BYTES));
+    return __builtin_bit_cast(v8i32, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else if constexpr (!LSM_TR_READ) {
+    static_assert(OT::mf16, "16 x 16 x 128 MN layout");
+    const int col = base + (lane & 15);
+    v8i32 f;
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+        v |= (uint32_t)*(const unsigned char *)(lds + mn16_chunk_offset(128 * kk + 32 * (lane >> 4) + 4 * w + b,
+                                                                          col / 16, OT::ROW_BYTES, 1) +
+                                                 (col & 15))
+             << (8 * b);
+      f[w] = (int)v;
+    }
+    return f;
+  } else {
+    // lds + frag16_tr8_offset(lane, base, kk, q, ROW_BYTES), computed as
+    // ((tile + 256*(base >> 8) + lane part) XOR 16*((base >> 4) & 15)) + the
+    // k-step and q rows, which equals it because the tile base (a multiple of
+    // 1 KiB) has bits 4-7 clear.
+    static_assert(OT::mf16 && OT::ROW_BYTES >= 256 && OT::ROW_BYTES % 256 == 0 && OT::BYTES % 1024 == 0,
+                  "16 x 16 x 128 MN layout, rows a multiple of 256 bytes");
+    const uint32_t tile = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
+    const uint32_t a = ((tile + 256 * (base >> 8) + (uint32_t)frag16_tr8_lane(lane, OT::ROW_BYTES)) ^
+                        (uint32_t)(16 * ((base >> 4) & 15))) +
+                       (uint32_t)(128 * kk * OT::ROW_BYTES);
+    v2i32 p[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      p[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(uintptr_t)(a + 8 * q * OT::ROW_BYTES));
+    const auto lo = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
+    const auto hi = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// 16 x 16 fragment of the input type.
+template <class OT, int IN>
+__device__ __forceinline__ typename InT<IN>::frag read_frag16_in(const char *lds, int lane, int base, int kk) {
+  if constexpr (IN == IN_E4M3)
+    return read_frag16_8<OT>(lds, lane, base, kk);
+  else
+    return read_frag16<OT>(lds, lane, base, kk);
 }
 
 // C is written with non-temporal stores: nothing in the kernel reads it back,

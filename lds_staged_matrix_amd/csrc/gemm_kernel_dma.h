@@ -106,15 +106,15 @@ __device__ __forceinline__ void dma_tile(i32x4 rs, uint32_t lds_tile, int wave, 
 // tile 0, or kOutOfRange when the chunk lies outside the matrix.
 //   K-contiguous:  row = M/N index (mn0 + row), inner = k
 //   MN-contiguous: row = k index, inner = M/N index (mn0 + inner)
-// `phase` = 1 gives the offset for the odd load rounds of a tile whose
-// swizzle period is two rounds (OT::LANE_OFFSETS == 2): the same row and
-// slot, with the swizzle of the row one round further on.
+// `phase` = 1 gives the offset for the load rounds with OT::round_phase(d) = 1
+// of a tile that takes two lane offsets (OT::LANE_OFFSETS == 2): the same row
+// and slot, with the swizzle of the row OT::PHASE_ROWS rows further on.
 template <class OT>
 __device__ __forceinline__ uint32_t dma_lane_offset(int tid, int mn0, int mn_ext, int64_t ld,
                                                     uint32_t bytes, int &inner_out, int phase = 0) {
   const int row = loader_row(tid, OT::ROW_BYTES);
   const int pchunk = loader_chunk(tid, OT::ROW_BYTES);
-  const int lchunk = pchunk ^ OT::swizzle(row + phase * OT::ROW_STEP);
+  const int lchunk = pchunk ^ OT::swizzle(row + phase * OT::PHASE_ROWS);
   const int inner = OT::EPC * lchunk;                 // first element of the chunk
   inner_out = inner;
   int64_t off;

@@ -36,16 +36,16 @@
 // handling through buffer range checks and the inline-assembly loads are
 // those of gemm_kernel_dma.h.
 //
-// MF selects the MFMA shape: 16 (v_mfma_f32_16x16x32, the library's 16-bit
-// instances: each wave's 128 x 64 block as 8 x 4 blocks of 16 x 16) or 32
-// (v_mfma_f32_32x32x16, an A/B build only, and the fp8 32x32x64 of the
-// library's 8-bit instances).  Both read the same LDS bytes per K tile.  On
-// MI355X, at its 1400 W socket limit on random operands, the 16 x 16 x 32
-// instruction spends less energy per flop (a quarter of the accumulator
-// register traffic per instruction for half the work), so the chip holds a
-// higher clock: 8192^3 bf16 runs about 5% faster with it.  Its transposed
-// reads need their own swizzle (mn16_swizzle in lds_layout.h), with a period
-// of two load rounds.
+// MF selects the MFMA shape: 16 (the library: v_mfma_f32_16x16x32 for 16-bit
+// and v_mfma_scale_f32_16x16x128_f8f6f4 for E4M3 inputs, each wave's 128 x 64
+// block as 8 x 4 blocks of 16 x 16) or 32 (v_mfma_f32_32x32x16 and
+// v_mfma_scale_f32_32x32x64_f8f6f4, an A/B build).  Both read the same LDS
+// bytes per K tile.  On MI355X, at its 1400 W socket limit on random
+// operands, the 16 x 16 instructions spend less energy per flop (a quarter of
+// the accumulator register traffic per instruction for half the work), so the
+// chip holds a higher clock: 8192^3 bf16 runs about 5% faster with them.
+// Their transposed reads need their own swizzles (mn16_swizzle and
+// mn16_swizzle8 in lds_layout.h), which take two lane offsets per loader.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,14 +73,15 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
     uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
-  static_assert(MF == 32 || (MF == 16 && IN != IN_E4M3), "16 x 16 MFMAs on 16-bit inputs only");
+  static_assert(MF == 32 || MF == 16, "32 x 32 or 16 x 16 MFMAs");
   using L = AccLayout<MF>;
   constexpr int LOADERS = T::NT / 2;                     // group 0 issues every load
   constexpr int ES = InT<IN>::ES;
-  constexpr int KSTEPS = T::BK / (MF == 32 ? InT<IN>::KSTEP : 32);   // MFMA k-steps per K tile
+  // MFMA k-steps per K tile (a 16 x 16 MFMA is twice as deep as a 32 x 32 one)
+  constexpr int KSTEPS = T::BK / (MF == 32 ? InT<IN>::KSTEP : 2 * InT<IN>::KSTEP);
   constexpr int FM = T::TM / MF, FN = T::TN / MF;        // MFMA blocks per wave
-  // With 16 x 16 x 32 MFMAs an MN-contiguous tile takes the layout of those
-  // fragments' transposed reads; its swizzle period is two load rounds.
+  // With 16 x 16 MFMAs an MN-contiguous tile takes the layout of those
+  // fragments' transposed reads, with two lane offsets per loader.
   using OA = OperandTile<T::BM, T::BK, LA, LOADERS, ES, MF == 16>;
   using OB = OperandTile<T::BN, T::BK, LB, LOADERS, ES, MF == 16>;
   constexpr int STAGE = OA::BYTES + OB::BYTES;
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   int a_inner, b_inner, unused;
   const uint32_t a_voff = dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, a_inner);
   const uint32_t b_voff = dma_lane_offset<OB>(tid & (LOADERS - 1), n0, N, ldb, b_bytes, b_inner);
-  // offsets of the odd load rounds (the same as the even ones unless the
-  // tile's swizzle period is two rounds)
+  // offsets of the load rounds of the second swizzle phase (the same as the
+  // first unless the tile takes two lane offsets)
   const uint32_t a_voff1 = OA::LANE_OFFSETS == 2
       ? dma_lane_offset<OA>(tid & (LOADERS - 1), m0, M, lda, a_bytes, unused, 1) : a_voff;
   const uint32_t b_voff1 = OB::LANE_OFFSETS == 2
@@ -123,8 +124,8 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   const int lwave = wave & 3;
 
   // Load d of K tile kt is round d of A (d < OA::LOADS) or round
-  // d - OA::LOADS of B.  Per K tile, the lane offsets of each operand's even
-  // and odd load rounds (a K-contiguous tile has one phase, and its chunks at
+  // d - OA::LOADS of B.  Per K tile, the lane offsets of each operand's two
+  // swizzle phases (a K-contiguous tile has one phase, and its chunks at
   // k >= K in the last, partial K tile read as zero through kOutOfRange).
   struct Voffs { uint32_t a[2], b[2]; };
   auto voffs = [&](int kt) {
@@ -139,11 +140,11 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   auto issue_one = [&](int kt, int d, const Voffs &v) {
     const uint32_t st = lds0 + (uint32_t)((kt & 1) * STAGE);
     if (d < OA::LOADS)
-      dma16(rsA, st + (uint32_t)((d * LOADERS + 64 * lwave) * 16), v.a[d & 1],
+      dma16(rsA, st + (uint32_t)((d * LOADERS + 64 * lwave) * 16), v.a[OA::round_phase(d)],
             (uint32_t)kt * a_kstep + d * a_round);
     else
       dma16(rsB, st + OA::BYTES + (uint32_t)(((d - OA::LOADS) * LOADERS + 64 * lwave) * 16),
-            v.b[(d - OA::LOADS) & 1], (uint32_t)kt * b_kstep + (d - OA::LOADS) * b_round);
+            v.b[OB::round_phase(d - OA::LOADS)], (uint32_t)kt * b_kstep + (d - OA::LOADS) * b_round);
   };
   auto issue = [&](int kt) {
     const Voffs v = voffs(kt);
@@ -199,9 +200,9 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
                 fb[kk][i - FM] = read_frag_in<OB, IN>(sB, lane, wn * T::TN + 32 * (i - FM), kk);
             } else {
               if (i < FM)
-                fa[kk][i] = read_frag16<OA>(sA, lane, wm * T::TM + 16 * i, kk);
+                fa[kk][i] = read_frag16_in<OA, IN>(sA, lane, wm * T::TM + 16 * i, kk);
               else
-                fb[kk][i - FM] = read_frag16<OB>(sB, lane, wn * T::TN + 16 * (i - FM), kk);
+                fb[kk][i - FM] = read_frag16_in<OB, IN>(sB, lane, wn * T::TN + 16 * (i - FM), kk);
             }
             if constexpr (LOAD) {
               // spread LOADS_PER_TILE loads evenly over the FRAGS fragment reads
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
             if constexpr (MF == 32)
               acc[i][j] = mfma_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
             else
-              acc[i][j] = mfma_16x16x32<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
+              acc[i][j] = mfma16_step<IN>(fa[kk][i], fb[kk][j], acc[i][j]);
           }
 #pragma unroll
       for (int i = 0; i < FM; i++)

@@ -8,8 +8,8 @@
 //    ds_read_b64_tr_b8 and their address functions), and each lane's
 //    fragment is returned;
 //  * the MFMA operand and accumulator layouts: one MFMA (16x16x32 or
-//    32x32x16 on 16-bit inputs, 32x32x64 on E4M3) on operand registers the
-//    host fills, with every accumulator register returned;
+//    32x32x16 on 16-bit inputs, 16x16x128 or 32x32x64 on E4M3) on operand
+//    registers the host fills, with every accumulator register returned;
 //  * the buffer range check the direct-to-LDS loads use for their edges:
 //    loads whose vector offset is in range and whose vector plus scalar
 //    offset is not, into registers and into LDS;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64) void frag_probe_kernel(const u32x4 *__restrict_
   __syncthreads();
   typename InT<IN>::frag f;
   if constexpr (MF == 16)
-    f = read_frag16<OT>(lds, lane, base, kk);
+    f = read_frag16_in<OT, IN>(lds, lane, base, kk);
   else
     f = read_frag_in<OT, IN>(lds, lane, base, kk);
   out[lane] = f;
@@ -66,6 +66,8 @@ using KC256_16 = OperandTile<256, 64, KC, 256, 2, 1>;
 using KC8 = OperandTile<256, 128, KC, 256, 1>;          // E4M3, 128-byte rows
 using MN8 = OperandTile<256, 128, MNC, 256, 1>;         // E4M3, 256-byte rows
 using MN8_128 = OperandTile<128, 128, MNC, 256, 1>;     // E4M3, 128-byte rows
+using KC8_16 = OperandTile<256, 128, KC, 256, 1, 1>;    // E4M3, 16x16x128 fragments
+using MN8_16 = OperandTile<256, 128, MNC, 256, 1, 1>;   // E4M3, 256-byte rows, 16x16x128 layout
 
 // ------------------------------------------------------------ MFMA layouts
 
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(const typename InT<IN>::
 #pragma unroll
   for (int r = 0; r < L::R; r++) acc[r] = 0.f;
   if constexpr (MF == 16)
-    acc = mfma_16x16x32<IN>(a[lane], b[lane], acc);
+    acc = mfma16_step<IN>(a[lane], b[lane], acc);
   else
     acc = mfma_step<IN>(a[lane], b[lane], acc);
 #pragma unroll
@@ -155,7 +157,8 @@ extern "C" {
 // Tile kinds of lsm_probe_frag.
 enum {
   PROBE_KC256 = 0, PROBE_KC64x128 = 1, PROBE_MN256 = 2, PROBE_MN128 = 3, PROBE_MN64 = 4,
-  PROBE_MN256_16 = 5, PROBE_KC256_16 = 6, PROBE_KC8 = 7, PROBE_MN8 = 8, PROBE_MN8_128 = 9
+  PROBE_MN256_16 = 5, PROBE_KC256_16 = 6, PROBE_KC8 = 7, PROBE_MN8 = 8, PROBE_MN8_128 = 9,
+  PROBE_KC8_16 = 10, PROBE_MN8_16 = 11
 };
 
 // Reads fragment (base, kk) of a tile image of `bytes` bytes; out receives
@@ -174,11 +177,14 @@ int lsm_probe_frag(int kind, const void *image, int bytes, int base, int kk, voi
     case PROBE_KC8: return launch_frag<KC8, IN_E4M3, 32>(image, bytes, base, kk, out, s);
     case PROBE_MN8: return launch_frag<MN8, IN_E4M3, 32>(image, bytes, base, kk, out, s);
     case PROBE_MN8_128: return launch_frag<MN8_128, IN_E4M3, 32>(image, bytes, base, kk, out, s);
+    case PROBE_KC8_16: return launch_frag<KC8_16, IN_E4M3, 16>(image, bytes, base, kk, out, s);
+    case PROBE_MN8_16: return launch_frag<MN8_16, IN_E4M3, 16>(image, bytes, base, kk, out, s);
     default: return -1;
   }
 }
 
-// One MFMA: shape 16 (v_mfma_f32_16x16x32) or 32 (v_mfma_f32_32x32x16, or
+// One MFMA: shape 16 (v_mfma_f32_16x16x32, or v_mfma_scale_f32_16x16x128_f8f6f4
+// with unit scales for in_type 2) or 32 (v_mfma_f32_32x32x16, or
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for in_type 2), input
 // type 0 bf16, 1 fp16, 2 E4M3.  a, b: 64 lanes x 16 bytes (32 for E4M3);
 // out: 4 or 16 registers x 64 lanes of fp32.
@@ -196,6 +202,9 @@ int lsm_probe_mfma(int shape, int in_type, const void *a, const void *b, float *
   else if (shape == 32 && in_type == IN_F16)
     hipLaunchKernelGGL((mfma_probe_kernel<IN_F16, 32>), dim3(1), dim3(64), 0, s, (const v8i16 *)a,
                        (const v8i16 *)b, out);
+  else if (shape == 16 && in_type == IN_E4M3)
+    hipLaunchKernelGGL((mfma_probe_kernel<IN_E4M3, 16>), dim3(1), dim3(64), 0, s, (const v8i32 *)a,
+                       (const v8i32 *)b, out);
   else if (shape == 32 && in_type == IN_E4M3)
     hipLaunchKernelGGL((mfma_probe_kernel<IN_E4M3, 32>), dim3(1), dim3(64), 0, s, (const v8i32 *)a,
                        (const v8i32 *)b, out);

@@ -90,6 +90,18 @@ __host__ __device__ constexpr int mn16_swizzle(int k, int row_bytes) {
   return (!LSM_LDS_SWIZZLE || row_bytes < 256) ? 0 : 2 * ((k & 3) | ((k >> 1) & 4));
 }
 
+// The same for 8-bit elements read by the transposed fragments of
+// v_mfma_scale_f32_16x16x128_f8f6f4.  Those fragments hold k = 32g .. 32g+31
+// in lane group g, eight k-rows per ds_read_b64_tr_b8, so one 32-lane phase
+// reads k-rows {k..k+7} and {k+32..k+39}, 16 bytes each.  The XOR
+// (k & 7) | ((k >> 2) & 8) puts those sixteen rows in the sixteen 16-byte
+// bank groups of the line.  It depends on k only through k & 7 and bit 5, so
+// a loader whose rounds are 16 rows apart needs one lane offset for rounds
+// 0, 1, 4, 5, ... and one for rounds 2, 3, 6, 7, ...
+__host__ __device__ constexpr int mn16_swizzle8(int k, int row_bytes) {
+  return (!LSM_LDS_SWIZZLE || row_bytes < 256) ? 0 : (k & 7) | ((k >> 2) & 8);
+}
+
 // Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
 __host__ __device__ constexpr int kc_chunk_offset(int row, int chunk, int row_bytes) {
   return row * row_bytes + 16 * (chunk ^ kc_swizzle(row, row_bytes));
@@ -102,8 +114,8 @@ __host__ __device__ constexpr int mn_chunk_offset(int k, int chunk, int row_byte
 
 // Byte offset of 16-byte chunk `chunk` of k-row `k` in an MN-contiguous tile
 // laid out for the 16 x 16 x 32 transposed reads.
-__host__ __device__ constexpr int mn16_chunk_offset(int k, int chunk, int row_bytes) {
-  return k * row_bytes + 16 * (chunk ^ mn16_swizzle(k, row_bytes));
+__host__ __device__ constexpr int mn16_chunk_offset(int k, int chunk, int row_bytes, int es = 2) {
+  return k * row_bytes + 16 * (chunk ^ (es == 2 ? mn16_swizzle(k, row_bytes) : mn16_swizzle8(k, row_bytes)));
 }
 
 // ---------------------------------------------------------------- loader
@@ -121,8 +133,8 @@ __host__ __device__ constexpr int loader_lds_offset(int id, int row_bytes, bool 
 }
 
 // The same for an MN-contiguous 16-bit tile in the 16 x 16 x 32 layout.
-__host__ __device__ constexpr int loader_lds_offset16(int id, int row_bytes) {
-  return mn16_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes);
+__host__ __device__ constexpr int loader_lds_offset16(int id, int row_bytes, int es = 2) {
+  return mn16_chunk_offset(loader_row(id, row_bytes), loader_chunk(id, row_bytes), row_bytes, es);
 }
 
 // ---------------------------------------------------------------- fragment reads
@@ -209,6 +221,36 @@ __host__ __device__ constexpr int frag_tr8_offset(int lane, int base, int kk, in
   return mn_chunk_offset(64 * kk + 32 * (lane >> 5) + 8 * q + ((lane & 15) >> 1),
                          (base + 16 * ((lane >> 4) & 1)) / 16, row_bytes, 1) +
          8 * (lane & 1);
+}
+
+// Fragments of v_mfma_scale_f32_16x16x128_f8f6f4 on 8-bit elements: lane l
+// holds operand row/column (l & 15) and 32 bytes, byte b standing for
+// k = 128*kk + 32*(l >> 4) + b (as for the 32 x 32 form, only A and B sharing
+// the numbering matters).
+//
+// K-contiguous: two ds_read_b128 per fragment, q = 0, 1 delivering bytes
+// 16q .. 16q + 15.  A 16-lane phase reads 16 consecutive rows at one logical
+// chunk.
+__host__ __device__ constexpr int frag16_kc8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return kc_chunk_offset(base + (lane & 15), 8 * kk + 2 * (lane >> 4) + q, row_bytes);
+}
+
+// MN-contiguous (rows of 256 bytes or more): four ds_read_b64_tr_b8 per
+// fragment, q = 0..3 delivering bytes 8q .. 8q + 7.  With the tr_b8 lane
+// exchange above, source lane s of group g (s' = s & 15) reads k-row
+// 128*kk + 32g + 8q + (s' >> 1) at columns base + 8*(s' & 1) .. +7, and
+// destination lane l ends with column base + (l & 15), k-rows
+// 128*kk + 32*(l >> 4) + 8q + 0..7.  The swizzle of those k-rows does not
+// depend on q or kk (k & 7 and bit 5 are fixed by the lane), so the address
+// is a lane part, XORed with the fragment's chunk on bits 4-7, plus
+// 8q + 128kk rows; frag16_tr8_offset is that sum.
+__host__ __device__ constexpr int frag16_tr8_lane(int lane, int row_bytes) {
+  const int k0 = 32 * (lane >> 4) + ((lane & 15) >> 1);   // the k-row, less 128*kk + 8q
+  return k0 * row_bytes + 16 * mn16_swizzle8(k0, row_bytes) + 8 * (lane & 1);
+}
+__host__ __device__ constexpr int frag16_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
+  return 256 * (base >> 8) + (frag16_tr8_lane(lane, row_bytes) ^ (16 * ((base >> 4) & 15))) +
+         (128 * kk + 8 * q) * row_bytes;
 }
 
 // ---------------------------------------------------------------- epilogue staging

@@ -13,6 +13,7 @@ libhw_probe.so.
     32x32x16:  lane l, element i: row/column l & 31, k = 16 kk + 8 (l >> 5) + i
     16x16x32:  lane l, element i: row/column l & 15, k = 32 kk + 8 (l >> 4) + i
     32x32x64 (E4M3): lane l, byte b: row/column l & 31, k = 64 kk + 32 (l >> 5) + b
+    16x16x128 (E4M3): lane l, byte b: row/column l & 15, k = 128 kk + 32 (l >> 4) + b
   This pins the transposed reads' lane exchange together with the address
   functions that rely on it.
 * MFMA layouts.  One MFMA on operands placed by those layouts must give
@@ -51,6 +52,8 @@ KINDS = {
     "KC8": (7, True, 256, 128, 1, 32),
     "MN8": (8, False, 128, 256, 1, 32),
     "MN8_128": (9, False, 128, 128, 1, 32),
+    "KC8_16": (10, True, 256, 128, 1, 16),
+    "MN8_16": (11, False, 128, 256, 1, 16),
 }
 
 
@@ -73,7 +76,7 @@ def probe():
 def layout():
     lib = ctypes.CDLL(hip_build.layout_host_path(""))
     for f in ("lsm_kc_chunk_offset", "lsm_mn_chunk_offset", "lsm_mn16_chunk_offset",
-              "lsm_mn_chunk_offset8"):
+              "lsm_mn_chunk_offset8", "lsm_mn16_chunk_offset8"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -91,10 +94,11 @@ def tile_image(layout, kc, rows, rb, es, mf16, tag_of):
         for c in range(rb // 16):
             if kc:
                 off = layout.lsm_kc_chunk_offset(r, c, rb)
+            elif mf16:
+                off = layout.lsm_mn16_chunk_offset(r, c, rb) if es == 2 else \
+                    layout.lsm_mn16_chunk_offset8(r, c, rb)
             elif es == 1:
                 off = layout.lsm_mn_chunk_offset8(r, c, rb)
-            elif mf16:
-                off = layout.lsm_mn16_chunk_offset(r, c, rb)
             else:
                 off = layout.lsm_mn_chunk_offset(r, c, rb)
             for e in range(epc):
@@ -115,7 +119,7 @@ def test_fragment_reads_deliver_the_mfma_operand_layout(probe, layout, name):
         tag = lambda r, e: e * bk + r          # outer = k, inner = x
     passes = [0] if es == 2 else [0, 1]        # one-byte elements: low, then high tag byte
     fw = 16 if mf == 16 else 32               # fragment width
-    kstep = {(2, 32): 16, (2, 16): 32, (1, 32): 64}[(es, mf)]
+    kstep = {(2, 32): 16, (2, 16): 32, (1, 32): 64, (1, 16): 128}[(es, mf)]
     per_lane = 8 if es == 2 else 32
     print(f"CASE fragment reads {name}", flush=True)
     got = {}
@@ -182,12 +186,13 @@ def run_mfma(probe, shape, in_type, A, B):
     return C
 
 
-MFMAS = [(32, 0), (32, 1), (16, 0), (16, 1), (32, 2)]     # (shape, input type)
+MFMAS = [(32, 0), (32, 1), (16, 0), (16, 1), (32, 2), (16, 2)]     # (shape, input type)
+DEPTH = {(32, 0): 16, (32, 1): 16, (16, 0): 32, (16, 1): 32, (32, 2): 64, (16, 2): 128}
 
 
 @pytest.mark.parametrize("shape,in_type", MFMAS)
 def test_mfma_layouts_random_integers(probe, shape, in_type):
-    K = {(32, 0): 16, (32, 1): 16, (16, 0): 32, (16, 1): 32, (32, 2): 64}[(shape, in_type)]
+    K = DEPTH[(shape, in_type)]
     rng = np.random.default_rng(100 + shape + in_type)
     print(f"CASE mfma {shape} input {in_type} random", flush=True)
     for _ in range(3):
@@ -197,10 +202,10 @@ def test_mfma_layouts_random_integers(probe, shape, in_type):
         assert np.array_equal(C, (A @ B).astype(np.float64))
 
 
-@pytest.mark.parametrize("shape,in_type", [(32, 0), (16, 0), (32, 2)])
+@pytest.mark.parametrize("shape,in_type", [(32, 0), (16, 0), (32, 2), (16, 2)])
 def test_mfma_layouts_one_hot(probe, shape, in_type):
     # A = e(i, k), B = e(k, j): C must be 1 at (i, j) and 0 elsewhere
-    K = {32: 16, 16: 32}[shape] if in_type != 2 else 64
+    K = DEPTH[(shape, in_type)]
     rng = np.random.default_rng(7)
     print(f"CASE mfma {shape} input {in_type} one-hot", flush=True)
     for i, k, j in [(0, 0, 0), (shape - 1, K - 1, shape - 1)] + \

@@ -1,7 +1,9 @@
-"""The A/B build of the ping-pong kernel on v_mfma_f32_32x32x16 (build
-variant "mfma32"), against the library (v_mfma_f32_16x16x32) and the oracle.
+"""The A/B build of the ping-pong kernel on the 32 x 32 MFMAs (build variant
+"mfma32": v_mfma_f32_32x32x16 for 16-bit and v_mfma_scale_f32_32x32x64_f8f6f4
+for E4M3 inputs), against the library (v_mfma_f32_16x16x32 and
+v_mfma_scale_f32_16x16x128_f8f6f4) and the oracle.
 
-The build changes only the MFMA shape of the 16-bit ping-pong kernel: its
+The build changes only the MFMA shape of the ping-pong kernel: its
 LDS layout of MN-contiguous tiles (the transposed-read swizzle of each
 fragment shape), fragment reads, accumulator layout and both epilogues (the
 LDS-staged one, taken when C rows are 16-byte aligned, and the direct one).
@@ -65,6 +67,30 @@ def test_mfma32_build_matches_the_library(variant, gd, la, lb):
         H.assert_canary(got, M, N, gd)
         bad = np.count_nonzero(got != lib_out)
         assert bad == 0, f"mfma32 build differs from the library in {bad} entries ({la}{lb}, ldc {ldc})"
+
+
+# E4M3: every extent a multiple of 16 bytes; K = 272 ends in a partial K tile
+# of 16 (BK 128).
+M8, N8, K8 = 4112, 4096, 272
+DTYPES8 = [lsm.GEMM_E4M3_F32, lsm.GEMM_E4M3_BF16]
+
+
+@pytest.mark.parametrize("gd", DTYPES8)
+@pytest.mark.parametrize("la,lb", ALL_LAYOUTS)
+def test_mfma32_build_matches_the_library_fp8(variant, gd, la, lb):
+    p = H.problem(M8, N8, K8, H.IN_OF[gd], la, lb, "int", (65, 66))
+    rows = [0, 1, 255, 256, 2047, 4095, 4096, 4111]
+    want = H.oracle_entries(p, np.repeat(rows, N8), np.tile(np.arange(N8), len(rows)))
+    want = want.reshape(len(rows), N8)
+    for ldc in (4096, 4097):   # C rows 16-byte aligned (LDS-staged epilogue) or not (direct)
+        print(f"CASE mfma32 fp8 {M8}x{N8}x{K8} {la}{lb} dtype {gd} ldc {ldc}", flush=True)
+        lib_out = H.run_gpu(p, gd, ldc=ldc, extra_rows=1)
+        H.assert_canary(lib_out, M8, N8, gd)
+        H.assert_exact(lib_out[rows, :N8], want, gd, f"library fp8 {la}{lb} ldc {ldc}")
+        got = H.run_gpu(p, gd, ldc=ldc, extra_rows=1, lib=variant)
+        H.assert_canary(got, M8, N8, gd)
+        bad = np.count_nonzero(got != lib_out)
+        assert bad == 0, f"mfma32 build differs from the library in {bad} entries (fp8 {la}{lb}, ldc {ldc})"
 
 
 def test_mfma32_build_real_inputs(variant):

@@ -116,7 +116,11 @@ def layouts():
                   "lsm_loader_lds_offset8", "lsm_frag_kc8_offset", "lsm_frag_tr8_offset",
                   "lsm_frag16_kc_offset", "lsm_frag16_tr_offset", "lsm_epi_stage_offset",
                   "lsm_mn16_swizzle", "lsm_mn16_chunk_offset", "lsm_loader_lds_offset16",
-                  "lsm_frag16_tr_lane"):
+                  "lsm_frag16_tr_lane", "lsm_mn16_swizzle8", "lsm_mn16_chunk_offset8",
+                  "lsm_loader_lds_offset16_8", "lsm_frag16_kc8_offset", "lsm_frag16_tr8_offset",
+                  "lsm_mn_chunk_offset8", "lsm_pp_mn_row_step", "lsm_pp_mn_loads",
+                  "lsm_pp_mn_lane_offsets", "lsm_pp_mn_phase_rows", "lsm_pp_mn_round_phase",
+                  "lsm_pp_mn_swizzle"):
             getattr(lib, f).restype = ctypes.c_int
         libs["swizzled" if s == "" else "linear"] = lib
     assert libs["swizzled"].lsm_layout_swizzled() == 1
@@ -403,6 +407,127 @@ def test_16x16_lds_image_gives_each_lane_its_mfma_operand(layouts, row_bytes):
                     frag[l] += v
             for l in range(64):
                 assert frag[l] == [(32 * kk + 8 * (l >> 4) + i, base + (l & 15)) for i in range(8)]
+
+
+# ------------------------------------------------------------------ 16 x 16 x 128 fragments, E4M3
+# (the ping-pong kernel on 8-bit inputs: lane l holds row/column l & 15 and 32
+# bytes, byte b standing for k = 128*kk + 32*(l >> 4) + b)
+
+def test_16x16_fp8_k_contig_reads_are_conflict_free_and_match_their_definition(layouts):
+    # two ds_read_b128 per fragment; a 16-lane phase reads 16 consecutive rows
+    # at one logical chunk (2 (l >> 4) + q of the 128-byte row)
+    lib = layouts["swizzled"]
+    rb = 128
+    for base in range(0, 256, 16):
+        for q in range(2):
+            addrs = [lib.lsm_frag16_kc8_offset(l, base, 0, q, rb) for l in range(64)]
+            assert degree(addrs, 16) == 1
+            for l in range(64):
+                assert addrs[l] == lib.lsm_kc_chunk_offset(base + (l & 15), 2 * (l >> 4) + q, rb)
+
+
+def tr8_16_read_degree(off, row_bytes, krows=128):
+    worst = 1
+    for base in range(0, row_bytes, 16):
+        for kk in range(krows // 128):
+            for q in range(4):
+                worst = max(worst, degree([off(l, base, kk, q, row_bytes) for l in range(64)], 8))
+    return worst
+
+
+@pytest.mark.parametrize("row_bytes", [256, 512])
+def test_16x16_fp8_transposed_reads_are_conflict_free(layouts, row_bytes):
+    # ds_read_b64_tr_b8: a 32-lane phase reads k-rows {k..k+7} and
+    # {k+32..k+39}, 16 bytes each; the swizzle puts the sixteen rows in the
+    # sixteen 16-byte bank groups of the line
+    assert tr8_16_read_degree(layouts["swizzled"].lsm_frag16_tr8_offset, row_bytes) == 1
+
+
+def test_16x16_fp8_transposed_reads_need_their_own_swizzle(layouts):
+    # the same reads on the 32 x 32 x 64 fragments' layout (XOR 2 (k & 7))
+    # put rows k and k + 32 on the same banks: 2-way; unswizzled, 16-way
+    lib = layouts["swizzled"]
+
+    def on_mn32_layout(l, base, kk, q, rb):
+        k = 128 * kk + 32 * (l >> 4) + 8 * q + ((l & 15) >> 1)
+        return lib.lsm_mn_chunk_offset8(k, base // 16, rb) + 8 * (l & 1)
+    assert tr8_16_read_degree(on_mn32_layout, 256) == 2
+    assert tr8_16_read_degree(layouts["linear"].lsm_frag16_tr8_offset, 256) == 16
+
+
+@pytest.mark.parametrize("row_bytes", [256, 512])
+def test_16x16_fp8_transposed_offset_matches_its_definition(layouts, row_bytes):
+    # frag16_tr8_offset is written as lane part XOR fragment bits (what the
+    # kernel evaluates); it must equal the plain definition: k-row
+    # 128 kk + 32 (l >> 4) + 8 q + ((l & 15) >> 1), chunk base / 16 of the
+    # 16 x 16 x 128 layout, byte 8 (l & 1) of the chunk
+    for name, lib in layouts.items():
+        for base in range(0, row_bytes, 16):
+            for kk in range(2):
+                for q in range(4):
+                    for l in range(64):
+                        k = 128 * kk + 32 * (l >> 4) + 8 * q + ((l & 15) >> 1)
+                        want = lib.lsm_mn16_chunk_offset8(k, base // 16, row_bytes) + 8 * (l & 1)
+                        assert lib.lsm_frag16_tr8_offset(l, base, kk, q, row_bytes) == want, name
+
+
+@pytest.mark.parametrize("es", [2, 1])
+def test_ping_pong_loader_lane_offsets_cover_every_round(layouts, es):
+    # The ping-pong kernel's loader keeps one lane offset per swizzle phase and
+    # picks one per load round (OperandTile::round_phase).  Right only if the
+    # swizzle of row r + d * step equals that of row r + phase(d) * PHASE_ROWS
+    # for every round d of the tile and every row r of a round.
+    lib = layouts["swizzled"]
+    step, loads = lib.lsm_pp_mn_row_step(es), lib.lsm_pp_mn_loads(es)
+    half = lib.lsm_pp_mn_phase_rows(es)
+    assert (step, loads, lib.lsm_pp_mn_lane_offsets(es)) == ((8, 8, 2) if es == 2 else (16, 8, 2))
+    for d in range(loads):
+        ph = lib.lsm_pp_mn_round_phase(es, d)
+        for r in range(step):
+            assert lib.lsm_pp_mn_swizzle(es, r + d * step) == lib.lsm_pp_mn_swizzle(es, r + ph * half)
+    # and one offset would not do: some round needs the second phase
+    assert any(lib.lsm_pp_mn_swizzle(es, r + d * step) != lib.lsm_pp_mn_swizzle(es, r)
+               for d in range(loads) for r in range(step))
+
+
+def tr8_redistribute(src):
+    """ds_read_b64_tr_b8 lane exchange on gfx950 (pinned on the GPU by the
+    hardware-map probe tests): inside each aligned group of 16 lanes,
+    destination lane d receives as byte j the byte d & 7 of source lane
+    (d >> 3) + 2 j.  `src` is the 64 lanes' 8-byte vectors."""
+    out = []
+    for d in range(64):
+        g = d & ~15
+        out.append([src[g + ((d & 15) >> 3) + 2 * j][d & 7] for j in range(8)])
+    return out
+
+
+@pytest.mark.parametrize("row_bytes", [256, 512])
+def test_16x16_fp8_lds_image_gives_each_lane_its_mfma_operand(layouts, row_bytes):
+    # Build the LDS image the loader writes (logical chunk c of k-row r at its
+    # swizzled place), read every fragment with frag16_tr8_offset and the lane
+    # exchange, and check that lane l ends with column base + (l & 15),
+    # k = 128 kk + 32 (l >> 4) + 0..31 -- the operand layout of
+    # v_mfma_scale_f32_16x16x128_f8f6f4.
+    lib = layouts["swizzled"]
+    width, krows = row_bytes, 128
+    image = {}
+    for cid in range(krows * row_bytes // 16):
+        r, c = cid // (row_bytes // 16), cid % (row_bytes // 16)
+        phys = lib.lsm_loader_lds_offset16_8(cid, row_bytes)
+        assert phys == lib.lsm_mn16_chunk_offset8(r, c, row_bytes)
+        for e in range(16):
+            image[phys + e] = (r, 16 * c + e)
+    assert len(image) == krows * width
+    for base in range(0, width, 16):
+        frag = [[] for _ in range(64)]
+        for q in range(4):
+            src = [[image[lib.lsm_frag16_tr8_offset(l, base, 0, q, row_bytes) + e] for e in range(8)]
+                   for l in range(64)]
+            for l, v in enumerate(tr8_redistribute(src)):
+                frag[l] += v
+        for l in range(64):
+            assert frag[l] == [(32 * (l >> 4) + b, base + (l & 15)) for b in range(32)]
 
 
 # ------------------------------------------------------------------ epilogue staging
