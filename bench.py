@@ -216,6 +216,91 @@ def lds_pad_probe(iters=4096, launches=50, repeats=9):
                       "results": res}), flush=True)
 
 
+
+def lds_read_patterns():
+    """(name, mode, 64 lane byte addresses) of the LDS read probe: the
+    kernels' own fragment-read addresses (through the host build of
+    lds_layout.h) and reference patterns.  Mode 0 ds_read_b64, 1
+    ds_read_b64_tr_b8, 2 ds_read_b128."""
+    import ctypes
+    from lds_staged_matrix_amd import build as hip_build
+    lay = ctypes.CDLL(hip_build.layout_host_path(""))
+    for f in ("lsm_kc_chunk_offset", "lsm_frag_kc_offset", "lsm_frag16_kc_offset", "lsm_frag_kc8_offset",
+              "lsm_frag16_kc8_offset", "lsm_frag_tr8_offset", "lsm_frag16_tr8_offset", "lsm_mn_chunk_offset8"):
+        getattr(lay, f).restype = ctypes.c_int
+    L = range(64)
+    pats = [("linear", 0, [8 * l for l in L]),
+            ("linear", 2, [16 * l for l in L]),
+            ("kc bf16 32x32 fragment", 2, [lay.lsm_frag_kc_offset(l, 0, 0, 128) for l in L]),
+            ("kc bf16 16x16 fragment", 2, [lay.lsm_frag16_kc_offset(l, 0, 0, 128) for l in L]),
+            ("kc e4m3 32x32 fragment", 2, [lay.lsm_frag_kc8_offset(l, 0, 0, 0, 128) for l in L]),
+            ("kc e4m3 16x16 fragment, chunks g and g+4 (library)", 2,
+             [lay.lsm_frag16_kc8_offset(l, 0, 0, 0, 128) for l in L]),
+            ("kc e4m3 16x16 fragment, chunks 2g and 2g+1", 2,
+             [lay.lsm_kc_chunk_offset(l & 15, 2 * (l >> 4), 128) for l in L]),
+            ("tr8 e4m3 32x32 fragment", 1, [lay.lsm_frag_tr8_offset(l, 0, 0, 0, 256) for l in L])]
+    for q in range(4):
+        pats.append((f"tr8 e4m3 16x16 fragment q{q} (library)", 1,
+                     [lay.lsm_frag16_tr8_offset(l, 0, 0, q, 256) for l in L]))
+    # the 16x16 reads on the 32x32 fragments' swizzle (rows k and k+16 on one bank)
+    pats.append(("tr8 e4m3 16x16 fragment on the 32x32 layout", 1,
+                 [lay.lsm_mn_chunk_offset8(16 * (l >> 4) + ((l & 15) >> 1), 0, 256) + 8 * (l & 1) for l in L]))
+    return pats
+
+
+def lds_read_probe(iters=2000, launches=2):
+    """One wave repeating one LDS read at given lane addresses
+    (libhw_probe.so lsm_probe_lds_read), `launches` launches per pattern in
+    the order printed, for counting bank conflicts per pattern with
+    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS.
+    Prints one JSON line with the patterns, the 4-byte-bank model's degree
+    (32-lane phases for 8-byte reads, 16-lane phases for 16-byte reads) and
+    the degree of the two-pass model of ds_read_b128."""
+    import ctypes
+    import torch
+    from lds_staged_matrix_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.HW_PROBE)
+    lib.lsm_probe_lds_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.lsm_probe_lds_read.restype = ctypes.c_int
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def degree_4b(addrs, width):
+        worst, per = 1, 256 // width
+        for p0 in range(0, 64, per):
+            banks = {}
+            for l in range(p0, p0 + per):
+                for dw in range(addrs[l] // 4, (addrs[l] + width) // 4):
+                    banks.setdefault(dw % 64, set()).add(dw)
+            worst = max(worst, max(len(v) for v in banks.values()))
+        return worst
+
+    def degree_b128_passes(addrs):
+        worst = 1
+        for lanes in (list(range(16)) + list(range(32, 48)), list(range(16, 32)) + list(range(48, 64))):
+            banks = {}
+            for l in lanes:
+                banks.setdefault((addrs[l] // 16) % 64, set()).add(addrs[l] // 16)
+            worst = max(worst, max(len(v) for v in banks.values()))
+        return worst
+
+    rows = []
+    for name, mode, addrs in lds_read_patterns():
+        arr = (ctypes.c_int * 64)(*addrs)
+        for _ in range(launches):
+            if lib.lsm_probe_lds_read(mode, arr, iters, out.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError(f"lsm_probe_lds_read refused pattern {name}")
+        torch.cuda.synchronize()
+        width = 16 if mode == 2 else 8
+        rows.append({"pattern": name, "instruction": ["ds_read_b64", "ds_read_b64_tr_b8", "ds_read_b128"][mode],
+                     "launches": launches, "reads_per_launch": iters,
+                     "model_way_4byte_banks": degree_4b(addrs, width),
+                     "model_way_b128_passes": degree_b128_passes(addrs) if mode == 2 else None})
+        log(f"lds read probe: {name} ({rows[-1]['instruction']})")
+    print(json.dumps({"probe": "lds lane-address reads, one wave", "results": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +329,8 @@ def main():
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
+    ap.add_argument("--lds-read-probe", action="store_true",
+                    help="LDS reads at chosen lane addresses (for the bank-conflict counters), then exit")
     ap.add_argument("--lds-pad-probe", action="store_true",
                     help="time the one-wave strided column read of a 64 x (64 + PAD) fp16 LDS "
                          "tile for PAD 0, 1, 2, 4, 32 (the padding table's probe), for "
@@ -280,6 +367,9 @@ def main():
         log(f"copy calibration: {n} bytes read, {n} bytes written")
         return
 
+    if args.lds_read_probe:
+        lds_read_probe()
+        return
     if args.lds_pad_probe:
         lds_pad_probe()
         return

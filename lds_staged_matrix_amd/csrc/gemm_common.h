@@ -100,12 +100,12 @@ struct OperandTile {
   static constexpr int LOADS = CHUNKS / NT;                      // 16-byte loads per thread
   static constexpr int ROW_STEP = NT / CPR;                      // rows between a thread's loads
   // rows per swizzle period
-  static constexpr int SWZ_PERIOD = kcontig ? 16 : mf16 ? (ES == 2 ? 16 : 64) : (ES == 2 ? 4 : 8);
+  static constexpr int SWZ_PERIOD = kcontig ? 16 : mf16 ? (ES == 2 ? 16 : 32) : (ES == 2 ? 4 : 8);
   // A thread's chunks of every load round share one swizzle phase when the
   // round step is a multiple of the period (one lane offset for all rounds).
   // The 16 x 16 MN layouts depend on the row only through the row inside a
   // round and one more bit, that of PHASE_ROWS (8 for 16-bit elements, rounds
-  // of 8 rows; 32 for 8-bit elements, rounds of 16 rows): one lane offset for
+  // of 8 rows; 16 for 8-bit elements, rounds of 16 rows): one lane offset for
   // the rounds with that bit clear and one for those with it set.
   static constexpr int PHASE_ROWS = SWZ_PERIOD / 2;
   static constexpr int LANE_OFFSETS = ROW_STEP % SWZ_PERIOD == 0 ? 1 : 2;
@@ -298,7 +298,8 @@ __device__ __forceinline__ v8i16 read_frag16(const char *lds, int lane, int base
 
 // One 16 x 128 operand fragment of v_mfma_scale_f32_16x16x128_f8f6f4 on
 // 8-bit elements (k-step kk of 128): lane l gets row/column (l & 15) of the
-// fragment starting at `base`, byte b standing for k = 128*kk + 32*(l >> 4) + b.
+// fragment starting at `base`, byte b standing for
+// k = 128*kk + 16*((l >> 4) + 4*(b >> 4)) + (b & 15) (frag16_kc8_offset).
 template <class OT>
 __device__ __forceinline__ v8i32 read_frag16_8(const char *lds, int lane, int base, int kk) {
   static_assert(OT::ES == 1, "8-bit tile");
@@ -315,7 +316,8 @@ __device__ __forceinline__ v8i32 read_frag16_8(const char *lds, int lane, int ba
       uint32_t v = 0;
 #pragma unroll
       for (int b = 0; b < 4; b++)
-        v |= (uint32_t)*(const unsigned char *)(lds + mn16_chunk_offset(128 * kk + 32 * (lane >> 4) + 4 * w + b,
+        v |= (uint32_t)*(const unsigned char *)(lds + mn16_chunk_offset(128 * kk + 16 * ((lane >> 4) + 4 * (w >> 2)) +
+                                                                              4 * (w & 3) + b,
                                                                           col / 16, OT::ROW_BYTES, 1) +
                                                  (col & 15))
              << (8 * b);
@@ -336,7 +338,8 @@ __device__ __forceinline__ v8i32 read_frag16_8(const char *lds, int lane, int ba
     v2i32 p[4];
 #pragma unroll
     for (int q = 0; q < 4; q++)
-      p[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(uintptr_t)(a + 8 * q * OT::ROW_BYTES));
+      p[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i32 *)(uintptr_t)(a + (uint32_t)(frag16_tr8_rows(0, q) * OT::ROW_BYTES)));
     const auto lo = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
     const auto hi = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

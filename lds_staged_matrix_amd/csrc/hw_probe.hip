@@ -15,7 +15,10 @@
 //    offset is not, into registers and into LDS;
 //  * a one-wave strided column read of a padded 64 x (64 + PAD) fp16 LDS
 //    tile ("Lds Optimization", "Optimization Method 2: Padding", the
-//    measured padding table), for calibrating the bank-conflict counters.
+//    measured padding table), for calibrating the bank-conflict counters;
+//  * one wave repeating one LDS read (ds_read_b64, ds_read_b64_tr_b8 or
+//    ds_read_b128) at 64 lane addresses the host chooses, so the counters can
+//    tell how the hardware groups a wave's lanes into bank passes.
 //
 // Built into libhw_probe.so next to the library; only the tests and the
 // benchmark's probe modes load it.  Every kernel runs one wave (64 threads)
@@ -142,6 +145,41 @@ __global__ __launch_bounds__(64) void pad_probe_kernel(int iters, float *__restr
   if (lane == 0) out[0] = acc;
 }
 
+// ------------------------------------------------------------ lane-address reads
+
+constexpr int kReadLds = 65536;   // LDS bytes of the read probe
+struct LaneAddrs { int a[64]; };
+
+// Fills the LDS with a counting pattern, then every lane repeats one read of
+// kind MODE (0 ds_read_b64, 1 ds_read_b64_tr_b8, 2 ds_read_b128) at its byte
+// address a[lane], `iters` times, each read's result folded into a sum that
+// lane writes to out[lane].  The host checks every address (in range and
+// aligned) before the launch.
+template <int MODE>
+__global__ __launch_bounds__(64) void read_probe_kernel(LaneAddrs addrs, int iters, int *__restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds[kReadLds];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < kReadLds / 4; i += 64) ((int *)lds)[i] = i;
+  __syncthreads();
+  int acc = 0;
+  for (int it = 0; it < iters; it++) {
+    int off = addrs.a[lane];
+    asm volatile("" : "+v"(off));   // opaque address: one read per iteration
+    if constexpr (MODE == 2) {
+      const u32x4 w = *(const u32x4 *)(lds + off);
+      acc += (int)(w[0] ^ w[1] ^ w[2] ^ w[3]);
+    } else {
+      v2i32 v;
+      if constexpr (MODE == 1)
+        v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(lds + off));
+      else
+        v = *(const lds_v2i32 *)(lds + off);
+      acc += v[0] ^ v[1];
+    }
+  }
+  out[lane] = acc;
+}
+
 template <class OT, int IN, int MF>
 int launch_frag(const void *image, int bytes, int base, int kk, void *out, hipStream_t s) {
   if (bytes != OT::BYTES || bytes > kImageMax || bytes % 16) return -1;
@@ -220,6 +258,27 @@ int lsm_probe_range(const void *buf, uint32_t num_records, uint32_t soff, void *
                     void *out_lds, hipStream_t s) {
   hipLaunchKernelGGL(range_probe_kernel, dim3(1), dim3(64), 0, s, buf, num_records, soff,
                      (u32x4 *)out_reg, (u32x4 *)out_lds);
+  return (int)hipGetLastError();
+}
+
+// Lane-address read probe: mode 0 ds_read_b64, 1 ds_read_b64_tr_b8, 2
+// ds_read_b128; addr: 64 host ints (byte addresses, 8-byte aligned, 16 for
+// mode 2, each read inside the 64 KiB probe LDS); out: 64 device ints.
+// Returns -1, launching nothing, for a bad mode or address.
+int lsm_probe_lds_read(int mode, const int *addr, int iters, int *out, hipStream_t s) {
+  LaneAddrs a;
+  const int width = mode == 2 ? 16 : 8;
+  if (mode < 0 || mode > 2 || iters < 0) return -1;
+  for (int l = 0; l < 64; l++) {
+    if (addr[l] < 0 || addr[l] % width != 0 || addr[l] + width > kReadLds) return -1;
+    a.a[l] = addr[l];
+  }
+  if (mode == 2)
+    hipLaunchKernelGGL(read_probe_kernel<2>, dim3(1), dim3(64), 0, s, a, iters, out);
+  else if (mode == 1)
+    hipLaunchKernelGGL(read_probe_kernel<1>, dim3(1), dim3(64), 0, s, a, iters, out);
+  else
+    hipLaunchKernelGGL(read_probe_kernel<0>, dim3(1), dim3(64), 0, s, a, iters, out);
   return (int)hipGetLastError();
 }
 

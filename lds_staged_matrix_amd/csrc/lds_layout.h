@@ -91,15 +91,15 @@ __host__ __device__ constexpr int mn16_swizzle(int k, int row_bytes) {
 }
 
 // The same for 8-bit elements read by the transposed fragments of
-// v_mfma_scale_f32_16x16x128_f8f6f4.  Those fragments hold k = 32g .. 32g+31
-// in lane group g, eight k-rows per ds_read_b64_tr_b8, so one 32-lane phase
-// reads k-rows {k..k+7} and {k+32..k+39}, 16 bytes each.  The XOR
-// (k & 7) | ((k >> 2) & 8) puts those sixteen rows in the sixteen 16-byte
-// bank groups of the line.  It depends on k only through k & 7 and bit 5, so
-// a loader whose rounds are 16 rows apart needs one lane offset for rounds
-// 0, 1, 4, 5, ... and one for rounds 2, 3, 6, 7, ...
+// v_mfma_scale_f32_16x16x128_f8f6f4.  Those fragments (frag16_tr8_offset)
+// hold k-rows 16g .. 16g+15 and 64+16g .. 64+16g+15 in lane group g, eight
+// k-rows per ds_read_b64_tr_b8, so one 32-lane phase reads k-rows
+// {k..k+7} and {k+16..k+23}, 16 bytes each.  The XOR (k & 7) | ((k >> 1) & 8)
+// puts those sixteen rows in the sixteen 16-byte bank groups of the line.  It
+// depends on k only through k & 7 and bit 4, so a loader whose rounds are 16
+// rows apart needs one lane offset for even and one for odd rounds.
 __host__ __device__ constexpr int mn16_swizzle8(int k, int row_bytes) {
-  return (!LSM_LDS_SWIZZLE || row_bytes < 256) ? 0 : (k & 7) | ((k >> 2) & 8);
+  return (!LSM_LDS_SWIZZLE || row_bytes < 256) ? 0 : (k & 7) | ((k >> 1) & 8);
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile.
@@ -224,33 +224,40 @@ __host__ __device__ constexpr int frag_tr8_offset(int lane, int base, int kk, in
 }
 
 // Fragments of v_mfma_scale_f32_16x16x128_f8f6f4 on 8-bit elements: lane l
-// holds operand row/column (l & 15) and 32 bytes, byte b standing for
-// k = 128*kk + 32*(l >> 4) + b (as for the 32 x 32 form, only A and B sharing
-// the numbering matters).
+// holds operand row/column (l & 15) and 32 bytes; as for the 32 x 32 form only
+// A and B sharing the numbering of k matters, and here byte b of lane group
+// g = l >> 4 stands for k = 128*kk + 16*(g + 4*(b >> 4)) + (b & 15): the
+// group's 16-byte chunks g and g + 4 of the 128-deep k step.
 //
 // K-contiguous: two ds_read_b128 per fragment, q = 0, 1 delivering bytes
-// 16q .. 16q + 15.  A 16-lane phase reads 16 consecutive rows at one logical
-// chunk.
+// 16q .. 16q + 15 (chunk g + 4q).  A 16-lane group reads 16 consecutive rows
+// at one logical chunk.  gfx950 serves a 64-lane ds_read_b128 in two passes
+// of 32 lanes, lanes 0-15 with 32-47 and 16-31 with 48-63, over 64 banks of
+// 16 bytes (measured with the bank-conflict counters); the groups that share
+// a pass read chunks g and g + 2, which the K-contiguous swizzle keeps apart.
+// (Chunks 2g + q would pair chunks c and c + 4, which the swizzle of rows
+// r and r + 8 maps onto one bank: 2-way.)
 __host__ __device__ constexpr int frag16_kc8_offset(int lane, int base, int kk, int q, int row_bytes) {
-  return kc_chunk_offset(base + (lane & 15), 8 * kk + 2 * (lane >> 4) + q, row_bytes);
+  return kc_chunk_offset(base + (lane & 15), 8 * kk + (lane >> 4) + 4 * q, row_bytes);
 }
 
 // MN-contiguous (rows of 256 bytes or more): four ds_read_b64_tr_b8 per
-// fragment, q = 0..3 delivering bytes 8q .. 8q + 7.  With the tr_b8 lane
-// exchange above, source lane s of group g (s' = s & 15) reads k-row
-// 128*kk + 32g + 8q + (s' >> 1) at columns base + 8*(s' & 1) .. +7, and
-// destination lane l ends with column base + (l & 15), k-rows
-// 128*kk + 32*(l >> 4) + 8q + 0..7.  The swizzle of those k-rows does not
-// depend on q or kk (k & 7 and bit 5 are fixed by the lane), so the address
-// is a lane part, XORed with the fragment's chunk on bits 4-7, plus
-// 8q + 128kk rows; frag16_tr8_offset is that sum.
+// fragment, q = 0..3 delivering bytes 8q .. 8q + 7, i.e. k-rows
+// 128*kk + 16g + 64*(q >> 1) + 8*(q & 1) + 0..7 of column base + (l & 15).
+// With the tr_b8 lane exchange above, source lane s of group g (s' = s & 15)
+// reads k-row 128*kk + 16g + 64*(q >> 1) + 8*(q & 1) + (s' >> 1) at columns
+// base + 8*(s' & 1) .. +7.  The swizzle of those k-rows does not depend on q
+// or kk (k & 7 and bit 4 are fixed by the lane), so the address is a lane
+// part, XORed with the fragment's chunk on bits 4-7, plus the q and kk rows;
+// frag16_tr8_offset is that sum.
 __host__ __device__ constexpr int frag16_tr8_lane(int lane, int row_bytes) {
-  const int k0 = 32 * (lane >> 4) + ((lane & 15) >> 1);   // the k-row, less 128*kk + 8q
+  const int k0 = 16 * (lane >> 4) + ((lane & 15) >> 1);   // the k-row, less the q and kk rows
   return k0 * row_bytes + 16 * mn16_swizzle8(k0, row_bytes) + 8 * (lane & 1);
 }
+__host__ __device__ constexpr int frag16_tr8_rows(int kk, int q) { return 128 * kk + 64 * (q >> 1) + 8 * (q & 1); }
 __host__ __device__ constexpr int frag16_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
   return 256 * (base >> 8) + (frag16_tr8_lane(lane, row_bytes) ^ (16 * ((base >> 4) & 15))) +
-         (128 * kk + 8 * q) * row_bytes;
+         frag16_tr8_rows(kk, q) * row_bytes;
 }
 
 // ---------------------------------------------------------------- epilogue staging

@@ -155,4 +155,5 @@ def test_probe_library_loads_and_exports_its_probes():
     out = subprocess.run(["nm", "-D", "--defined-only", hip_build.HW_PROBE], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
-    assert {"lsm_probe_frag", "lsm_probe_mfma", "lsm_probe_range", "lsm_probe_pad"} <= exported
+    assert {"lsm_probe_frag", "lsm_probe_mfma", "lsm_probe_range", "lsm_probe_pad",
+            "lsm_probe_lds_read"} <= exported

@@ -13,7 +13,8 @@ libhw_probe.so.
     32x32x16:  lane l, element i: row/column l & 31, k = 16 kk + 8 (l >> 5) + i
     16x16x32:  lane l, element i: row/column l & 15, k = 32 kk + 8 (l >> 4) + i
     32x32x64 (E4M3): lane l, byte b: row/column l & 31, k = 64 kk + 32 (l >> 5) + b
-    16x16x128 (E4M3): lane l, byte b: row/column l & 15, k = 128 kk + 32 (l >> 4) + b
+    16x16x128 (E4M3): lane l, byte b: row/column l & 15,
+                      k = 128 kk + 16 ((l >> 4) + 4 (b >> 4)) + (b & 15)
   This pins the transposed reads' lane exchange together with the address
   functions that rely on it.
 * MFMA layouts.  One MFMA on operands placed by those layouts must give
@@ -141,8 +142,13 @@ def test_fragment_reads_deliver_the_mfma_operand_layout(probe, layout, name):
     for (base, kk), v in got.items():
         for l in range(64):
             x = base + (l & (fw - 1))
-            k0 = kstep * kk + (per_lane if es == 2 else 32) * (l // fw)
-            want = [x * bk + k0 + i for i in range(per_lane)]
+            if (es, mf) == (1, 16):
+                # 16x16x128: byte b of group g is k = 16 (g + 4 (b >> 4)) + (b & 15)
+                ks = [kstep * kk + 16 * ((l >> 4) + 4 * (b >> 4)) + (b & 15) for b in range(32)]
+            else:
+                k0 = kstep * kk + (per_lane if es == 2 else 32) * (l // fw)
+                ks = [k0 + i for i in range(per_lane)]
+            want = [x * bk + k for k in ks]
             assert list(v[l]) == want, (name, base, kk, l)
 
 
@@ -256,3 +262,24 @@ def test_padded_column_probe_runs(probe):
         torch.cuda.synchronize()
         assert float(out.item()) == 0.0
     assert probe.lsm_probe_pad(3, 100, out.data_ptr(), stream()) == -1
+
+
+def test_lane_address_read_probe_runs_and_refuses_bad_addresses(probe):
+    # the bank-pass probe of ds_read_b64 / _tr_b8 / _b128: every mode runs on
+    # in-range addresses and returns the fold of what it read; addresses out
+    # of range or misaligned are refused on the host with nothing launched
+    probe.lsm_probe_lds_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    probe.lsm_probe_lds_read.restype = ctypes.c_int
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for mode, width in ((0, 8), (1, 8), (2, 16)):
+        good = (ctypes.c_int * 64)(*[width * l for l in range(64)])
+        assert probe.lsm_probe_lds_read(mode, good, 3, out.data_ptr(), stream()) == 0
+        torch.cuda.synchronize()
+        if mode == 0:
+            # LDS holds dword i at byte 4 i; lane l folds (2 l) ^ (2 l + 1) = 1, three times
+            assert out.cpu().tolist() == [3] * 64
+    for bad in ([65536 - 8] + [0] * 63, [4] + [0] * 63, [-16] + [0] * 63):
+        arr = (ctypes.c_int * 64)(*bad)
+        assert probe.lsm_probe_lds_read(2, arr, 3, out.data_ptr(), stream()) == -1
+    assert probe.lsm_probe_lds_read(3, (ctypes.c_int * 64)(), 3, out.data_ptr(), stream()) == -1
