@@ -623,6 +623,7 @@ def test_epilogue_staging_writes_and_reads_are_conflict_free(layouts, mf, esz):
     for it in range(64 * cpr // 64):
         addrs = [off(it * (64 // cpr) + lane // cpr, lane % cpr) for lane in range(64)]
         assert degree(addrs, 16) == 1
+        assert b128_degree(addrs) == 1        # and in the measured two-pass form of ds_read_b128
 
 
 @pytest.mark.parametrize("mf", [32, 16])
