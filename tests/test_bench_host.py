@@ -57,3 +57,27 @@ def test_cpu_baseline_times_the_oracle_on_a_sample():
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "rows 0..7" in r["sample"]
+
+
+def test_lds_read_probe_patterns_are_in_range_and_aligned():
+    # bench.py --lds-read-probe hands these to the probe kernel, whose host
+    # entry refuses anything outside its 64 KiB LDS or misaligned; every
+    # pattern must pass that check, and every mode must be one it knows
+    pats = bench.lds_read_patterns()
+    assert len({(n, m) for n, m, _ in pats}) == len(pats)
+    for name, mode, addrs in pats:
+        width = 16 if mode == 2 else 8
+        assert mode in (0, 1, 2) and len(addrs) == 64, name
+        assert all(0 <= a and a % width == 0 and a + width <= 65536 for a in addrs), name
+
+
+def test_lds_read_probe_patterns_cover_the_measured_cases():
+    # the profile's table pins the two-pass form of ds_read_b128 with the
+    # kernels' own fragment reads and the one pattern that tells the models
+    # apart (chunks 2g, 2g + 1 of 16 consecutive 128-byte rows)
+    names = {n for n, _, _ in bench.lds_read_patterns()}
+    assert "kc e4m3 16x16 fragment, chunks 2g and 2g+1" in names
+    assert "kc e4m3 16x16 fragment, chunks g and g+4 (library)" in names
+    text = open(os.path.join(ROOT, "profiles", "lds_bank_passes_read_probe.txt")).read()
+    for n in names:
+        assert n in text, n
