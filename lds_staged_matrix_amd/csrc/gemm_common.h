@@ -47,10 +47,11 @@ enum { KC = 0, MNC = 1 };                       // operand contiguity, values of
 enum { IN_BF16 = 0, IN_F16 = 1, IN_E4M3 = 2 };
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
-// Input element types: bytes per element, k per MFMA and the per-lane
-// operand fragment.  16-bit inputs use v_mfma_f32_32x32x16_{bf16,f16} (8
-// elements, 16 bytes per lane); OCP fp8 E4M3 inputs use
-// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (32 elements, 32 bytes).
+// Input element types: bytes per element, k per 32 x 32 MFMA and the per-lane
+// operand fragment.  16-bit inputs use v_mfma_f32_32x32x16_{bf16,f16} or
+// v_mfma_f32_16x16x32_{bf16,f16} (8 elements, 16 bytes per lane; k = KSTEP or
+// 2*KSTEP); OCP fp8 E4M3 inputs use v_mfma_scale_f32_32x32x64_f8f6f4 or
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (32 elements, 32 bytes).
 template <int IN>
 struct InT {
   static constexpr int ES = 2, KSTEP = 16;
