@@ -17,6 +17,7 @@ import torch
 import lds_staged_matrix_amd as lsm
 import synth
 import gpu_harness as H
+from test_gpu_parity import every_tile_check
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +91,18 @@ def test_fp8_workload_8192_nn_f32():
     rows, cols = rng.integers(0, 8192, 2000), rng.integers(0, 8192, 2000)
     H.assert_close(C[rows, cols], H.oracle_entries(p, rows, cols), 8192, lsm.GEMM_E4M3_F32,
                    "entries")
+    # a full row in every tile row and a full column in every tile column:
+    # every 256 x 256 tile of the launch has checked entries
+    every_tile_check(p, C, lsm.GEMM_E4M3_F32, False, seed=7)
+
+
+def test_fp8_workload_8192_integer_exact_every_tile():
+    # the workload's integer variant (values -2..2, exact in E4M3 and in the
+    # fp32 sums): the unique result, bit for bit, in every tile
+    print("CASE fp8 8192 int", flush=True)
+    p = H.problem(8192, 8192, 8192, synth.E4M3, "K", "MN", "int", (6001, 6002))
+    C = H.run_gpu(p, lsm.GEMM_E4M3_F32)
+    every_tile_check(p, C, lsm.GEMM_E4M3_F32, True, seed=8)
 
 
 def test_fp8_k_zero_writes_zeros():
