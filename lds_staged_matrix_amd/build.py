@@ -35,6 +35,7 @@ VARIANTS = {
     "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
     "mfma32": ["-DLSM_PP_MFMA=32", "-DLSM_PP_MFMA8=32"],   # ping-pong kernel on 32x32 MFMAs (32x32x16, fp8 32x32x64)
     "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
+    "waveepi": ["-DLSM_PP_ROW_EPI=0"],      # ping-pong: C staged per wave (256/128-byte pieces) instead of per workgroup
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

@@ -486,6 +486,76 @@ __device__ __forceinline__ void epilogue_lds(void *C,
   }
 }
 
+// Workgroup-row epilogue (the ping-pong kernel's): the whole workgroup
+// stages C through LDS, RP = LDS_BYTES / (BN * sizeof(out)) rows at a time,
+// so that each 64-lane store writes whole rows of the workgroup tile (1 KiB
+// of fp32, or two 512-byte rows of bf16/fp16) instead of the 256- or
+// 128-byte pieces of one wave's tile that epilogue_lds stores.  The waves
+// whose rows a pass holds write their accumulators (epi_row_stage_offset in
+// lds_layout.h: every write and every 16-byte read conflict-free); after a
+// barrier every wave reads and stores RP / waves rows; a barrier ends the
+// pass.  Called by every wave of the workgroup, with the LDS free.  On MI355X
+// it measured 0.2-0.8% faster than epilogue_lds in the ping-pong kernel
+// (bf16 8192^3, 4096^3 with bf16 output, E4M3 8192^3; bit-exact).
+template <class T, int OUT, int LDS_BYTES, int MF>
+__device__ __forceinline__ void epilogue_lds_rows(void *C,
+                                                  const typename AccLayout<MF>::type (&acc)[T::TM / MF][T::TN / MF],
+                                                  char *lds, int M, int N, int64_t ldc, int m0, int n0,
+                                                  int wm, int wn, int wave, int lane) {
+  using L = AccLayout<MF>;
+  typedef typename OutElem<OUT>::type E;
+  constexpr int ESZ = sizeof(E);
+  constexpr int WROWB = T::BN * ESZ;                      // bytes of one workgroup-tile row
+  constexpr int CPR = WROWB / 16;                         // 16-byte chunks per row
+  constexpr int RP = LDS_BYTES / WROWB < T::BM ? LDS_BYTES / WROWB : T::BM;   // rows per pass
+  constexpr int WAVES = T::WM * T::WN;
+  constexpr int RPW = RP / WAVES;                         // rows each wave stores per pass
+  constexpr int RPI = 64 / CPR >= 1 ? 64 / CPR : 1;       // rows per 64-lane read
+  static_assert(RP % T::TM == 0 && RP * WROWB <= LDS_BYTES && CPR <= 64 && 64 % CPR == 0 &&
+                RPW % RPI == 0, "workgroup-row staging geometry");
+  auto off = [&](int row, int chunk) { return epi_row_stage_offset(row, chunk, WROWB, MF, ESZ); };
+  if constexpr (LSM_LDS_POISON) {   // poison build: the staging region, before its writes
+    lds_poison(lds, RP * WROWB, wave * 64 + lane, WAVES * 64);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int pass = 0; pass < T::BM / RP; pass++) {
+    if (wm * T::TM >= pass * RP && wm * T::TM < (pass + 1) * RP) {
+#pragma unroll
+      for (int i = 0; i < T::TM / MF; i++)
+#pragma unroll
+        for (int j = 0; j < T::TN / MF; j++)
+#pragma unroll
+          for (int r = 0; r < L::R; r++) {
+            const int row = wm * T::TM - pass * RP + MF * i + L::row(r, lane);
+            const int col = wn * T::TN + MF * j + L::col(lane);
+            *(E *)(lds + off(row, col * ESZ / 16) + (col * ESZ) % 16) = (E)acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < RPW / RPI; it++) {
+      const int row = wave * RPW + it * RPI + lane / CPR;
+      const int chunk = lane % CPR;
+      const u32x4 v = *(const u32x4 *)(lds + off(row, chunk));
+      const int grow = m0 + pass * RP + row;
+      const int gcol = n0 + chunk * (16 / ESZ);
+      if (grow < M) {
+        E *dst = (E *)C + (int64_t)grow * ldc + gcol;
+        if (gcol + 16 / ESZ <= N) {
+          __builtin_nontemporal_store(v, (u32x4 *)dst);
+        } else {
+          const E *e = (const E *)&v;
+#pragma unroll
+          for (int q = 0; q < 16 / ESZ; q++)
+            if (gcol + q < N) __builtin_nontemporal_store(e[q], dst + q);
+        }
+      }
+    }
+    if (pass + 1 < T::BM / RP) __syncthreads();
+  }
+}
+
 // Operand fragment for input type IN (k-step kk of the tile).
 template <class OT, int IN>
 __device__ __forceinline__ typename InT<IN>::frag read_frag_in(const char *lds, int lane, int base,

@@ -58,6 +58,13 @@
 
 namespace lsm {
 
+// The library stages C through LDS for the whole workgroup at once
+// (epilogue_lds_rows); LSM_PP_ROW_EPI = 0, an A/B build only, stages it per
+// wave (epilogue_lds) instead.
+#ifndef LSM_PP_ROW_EPI
+#define LSM_PP_ROW_EPI 1
+#endif
+
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -257,7 +264,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   // The LDS is free once every wave is past its last fragment read.
   if (c_vec) {
     __syncthreads();
-    epilogue_lds<T, OUT, 2 * STAGE, MF>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+    if constexpr (LSM_PP_ROW_EPI)
+      epilogue_lds_rows<T, OUT, 2 * STAGE, MF>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+    else
+      epilogue_lds<T, OUT, 2 * STAGE, MF>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
   } else {
     epilogue<T, OUT, MF>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
   }

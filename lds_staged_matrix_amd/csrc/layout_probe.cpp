@@ -50,6 +50,9 @@ int lsm_frag_tr8_offset(int lane, int base, int kk, int q, int row_bytes) {
   return lsm::frag_tr8_offset(lane, base, kk, q, row_bytes);
 }
 int lsm_mn16_swizzle8(int k, int row_bytes) { return lsm::mn16_swizzle8(k, row_bytes); }
+int lsm_epi_row_stage_offset(int row, int chunk, int row_bytes, int mf, int esz) {
+  return lsm::epi_row_stage_offset(row, chunk, row_bytes, mf, esz);
+}
 int lsm_mn16_chunk_offset8(int k, int chunk, int row_bytes) {
   return lsm::mn16_chunk_offset(k, chunk, row_bytes, 1);
 }

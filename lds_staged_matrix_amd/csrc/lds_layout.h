@@ -278,6 +278,19 @@ __host__ __device__ constexpr int epi_stage_offset(int row, int chunk, int row_b
                                                    : ((row >> 2) & 3) * (row_bytes / 64)));
 }
 
+// The ping-pong kernel's workgroup-row staging (epilogue_lds_rows): rows of
+// the whole workgroup tile, `row_bytes` each, written by the MFMA
+// accumulator layout of block size `mf` with `esz`-byte elements and read
+// back 16 bytes per lane.  One 16 x 16 accumulator write covers rows r, r + 4,
+// r + 8 and r + 12 at 16 consecutive columns (16 * esz bytes); a 32 x 32 one
+// rows r and r + 4 at 32 columns.  The chunk XOR ((row >> 2) & 3) * esz
+// (16 x 16) or ((row >> 2) & 1) * 2 * esz (32 x 32) moves each of those row
+// groups to its own bank range; it stays below 16, so it permutes the chunks
+// inside each 256-byte piece of a row and whole-row reads stay conflict-free.
+__host__ __device__ constexpr int epi_row_stage_offset(int row, int chunk, int row_bytes, int mf, int esz) {
+  return row * row_bytes + 16 * (chunk ^ (mf == 16 ? ((row >> 2) & 3) * esz : ((row >> 2) & 1) * 2 * esz));
+}
+
 // ---------------------------------------------------------------- workgroup -> tile
 //
 // Workgroups are handed to the 8 XCDs round-robin (workgroup b on XCD b mod 8),

@@ -2,7 +2,8 @@
 16-bit reads instead of ds_read_b64_tr_b16, a 2-stage ring for M <= 32,
 tiles in hardware workgroup order instead of the per-XCD order, one LDS
 stage instead of two in the direct-to-LDS kernel, the 64 x 64 tile without
-its four-stage pipeline, 32 x 32 x 16 MFMAs in the ping-pong kernel)
+its four-stage pipeline, 32 x 32 MFMAs in the ping-pong kernel, the
+ping-pong kernel staging C per wave instead of per workgroup)
 compute the same products: bit-identical to the library on integer-valued
 inputs, whose result is unique.  Their speed and counters are what the
 benchmark compares; this checks that they are the same computation."""
@@ -16,7 +17,7 @@ import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1", "small2", "mfma32"]
+VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1", "small2", "mfma32", "waveepi"]
 # one shape per kernel: ping-pong (>= 256 tiles of 256), 128 x 128 tile
 # (>= 256 tiles of 128), 64 x 64 tile with two and with four LDS stages (its
 # operand panels beyond one XCD's L2), split-K ring (M <= 32)

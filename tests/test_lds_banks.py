@@ -120,7 +120,7 @@ def layouts():
                   "lsm_loader_lds_offset16_8", "lsm_frag16_kc8_offset", "lsm_frag16_tr8_offset",
                   "lsm_mn_chunk_offset8", "lsm_pp_mn_row_step", "lsm_pp_mn_loads",
                   "lsm_pp_mn_lane_offsets", "lsm_pp_mn_phase_rows", "lsm_pp_mn_round_phase",
-                  "lsm_pp_mn_swizzle"):
+                  "lsm_pp_mn_swizzle", "lsm_epi_row_stage_offset"):
             getattr(lib, f).restype = ctypes.c_int
         libs["swizzled" if s == "" else "linear"] = lib
     assert libs["swizzled"].lsm_layout_swizzled() == 1
@@ -624,6 +624,46 @@ def test_epilogue_staging_writes_and_reads_are_conflict_free(layouts, mf, esz):
         addrs = [off(it * (64 // cpr) + lane // cpr, lane % cpr) for lane in range(64)]
         assert degree(addrs, 16) == 1
         assert b128_degree(addrs) == 1        # and in the measured two-pass form of ds_read_b128
+
+
+# The ping-pong kernel's workgroup-row staging: rows of the 256-column
+# workgroup tile (1 KiB of fp32, 512 bytes of bf16/fp16), written by every
+# accumulator register of the tile's waves, read back 16 bytes per lane.
+
+@pytest.mark.parametrize("mf", [32, 16])
+@pytest.mark.parametrize("esz", [4, 2])
+def test_workgroup_row_staging_is_conflict_free(layouts, mf, esz):
+    lib = layouts["swizzled"]
+    rowb, tm, tn = 256 * esz, 128, 64
+    rp = min(2 * 65536 // rowb, 256)                       # rows per pass in 128 KiB
+    off = lambda row, chunk: lib.lsm_epi_row_stage_offset(row, chunk, rowb, mf, esz)
+    for wm in range(rp // tm):                             # the waves of one pass
+        for wn in range(4):
+            for i in range(tm // mf):
+                for j in range(tn // mf):
+                    for r in range(16 if mf == 32 else 4):
+                        addrs = []
+                        for lane in range(64):
+                            row, col = acc_row_col(mf, r, lane)
+                            row, col = wm * tm + row + mf * i, wn * tn + col + mf * j
+                            a = off(row, col * esz // 16) + (col * esz) % 16
+                            assert 0 <= a < rp * rowb
+                            addrs.append(a)
+                        assert degree(addrs, esz) == 1, (wm, wn, i, j, r)
+    cpr = rowb // 16
+    for base in range(0, rp, max(64 // cpr, 1)):
+        addrs = [off(base + lane // cpr, lane % cpr) for lane in range(64)]
+        assert degree(addrs, 16) == 1 and b128_degree(addrs) == 1
+
+
+@pytest.mark.parametrize("mf", [32, 16])
+@pytest.mark.parametrize("esz", [4, 2])
+def test_workgroup_row_staging_is_a_permutation_of_each_row(layouts, mf, esz):
+    lib = layouts["swizzled"]
+    rowb = 256 * esz
+    for row in range(256):
+        got = sorted(lib.lsm_epi_row_stage_offset(row, c, rowb, mf, esz) for c in range(rowb // 16))
+        assert got == [row * rowb + 16 * c for c in range(rowb // 16)]
 
 
 @pytest.mark.parametrize("mf", [32, 16])
