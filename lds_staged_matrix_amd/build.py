@@ -36,6 +36,7 @@ VARIANTS = {
     "mfma32": ["-DLSM_PP_MFMA=32", "-DLSM_PP_MFMA8=32"],   # ping-pong kernel on 32x32 MFMAs (32x32x16, fp8 32x32x64)
     "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
     "waveepi": ["-DLSM_PP_ROW_EPI=0"],      # ping-pong: C staged per wave (256/128-byte pieces) instead of per workgroup
+    "oneloader": ["-DLSM_PP_SPLIT_LOADS=0"],  # ping-pong: group 0 issues every load, for every layout (no split, 2 B stages)
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}
