@@ -37,9 +37,10 @@
 //    So each group issues half of the 64 KiB of loads per tile, in its own
 //    memory phase, and the B loads have three phases to land.
 //  * one loader (A MN-contiguous, TN and TT, where splitting measured
-//    slower): group 0 loads all of tile t+1 in M(t), into two stages of
-//    64 KiB; it waits for them before barrier 2t+2.  The loads have two
-//    phases to land, and group 0's memory phase carries all of them.
+//    slower; and the A/B builds that change the fragment reads): group 0
+//    loads all of tile t+1 in M(t), into two stages of 64 KiB; it waits for
+//    them before barrier 2t+2.  The loads have two phases to land, and
+//    group 0's memory phase carries all of them.
 // Tiles 0 and 1 come with the prologue (split: each group its operand).
 // Every wave waits for its own LDS reads before the barrier that ends its
 // memory phase, and a tile is complete at the barrier before its first read.
@@ -116,11 +117,14 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   // Load schedule (see the head of this file): one loader group, or the
   // loads split between the groups -- compiled per group, or in one memory
   // phase whose operand each wave selects (B K-contiguous: the per-group
-  // form needs more than 256 VGPRs there).
+  // form needs more than 256 VGPRs there).  The A/B builds that change the
+  // fragment reads (32 x 32 MFMAs, no swizzle, scalar 16-bit reads) keep one
+  // loader group: with them both split forms need more.
   enum { ONE_LOADER, SPLIT_SELECT, SPLIT_PER_GROUP };
-  constexpr int SCHED = !LSM_PP_SPLIT_LOADS || LA != KC ? ONE_LOADER
-                        : LB == MNC                     ? SPLIT_PER_GROUP
-                                                        : SPLIT_SELECT;
+  constexpr bool SPLIT_FITS = MF == 16 && LSM_LDS_SWIZZLE && LSM_TR_READ;
+  constexpr int SCHED = !LSM_PP_SPLIT_LOADS || LA != KC || !SPLIT_FITS ? ONE_LOADER
+                        : LB == MNC                                    ? SPLIT_PER_GROUP
+                                                                       : SPLIT_SELECT;
   constexpr bool SPLIT = SCHED != ONE_LOADER;
   // A stages, then B stages (two each, or three of B when the loads are split)
   constexpr int A_STAGE = SPLIT ? OA::BYTES : STAGE;
