@@ -3,7 +3,8 @@
 tiles in hardware workgroup order instead of the per-XCD order, one LDS
 stage instead of two in the direct-to-LDS kernel, the 64 x 64 tile without
 its four-stage pipeline, 32 x 32 MFMAs in the ping-pong kernel, the
-ping-pong kernel staging C per wave instead of per workgroup)
+ping-pong kernel staging C per wave instead of per workgroup, the ping-pong
+kernel with one loader group instead of loads split between its groups)
 compute the same products: bit-identical to the library on integer-valued
 inputs, whose result is unique.  Their speed and counters are what the
 benchmark compares; this checks that they are the same computation."""
