@@ -325,7 +325,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--variant", default=None,
                     help="benchmark an A/B build that changes one design choice "
-                         "(noswizzle, scalar_tr, ring2, noxcd, stage1, small2, mfma32) instead of the library")
+                         "(noswizzle, scalar_tr, ring2, noxcd, stage1, small2, mfma32, poison, waveepi, "
+                         "oneloader) instead of the library")
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
