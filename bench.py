@@ -217,6 +217,84 @@ def lds_pad_probe(iters=4096, launches=50, repeats=9):
 
 
 
+def phase_timeline(launches=100, settle_ms=600.0):
+    """Where the ping-pong kernel's cycles go, 8192^3 NN bf16 -> fp32 on the
+    workload's inputs: the measurement builds `timeline` (the library's
+    schedule) and `timeline1` (one loader group) add up, per wave, the
+    shader-clock cycles of each phase over the K loop (see LSM_PP_TIMELINE in
+    gemm_kernel_pingpong.h).  Each build runs `settle_ms` of launches, then
+    `launches` timed ones (HIP events); the counts are those of the last
+    launch.  Its C is checked bit for bit against the library's.  Prints the
+    table and one JSON line."""
+    import ctypes
+    import torch
+    import lds_staged_matrix_amd as lsm
+    from lds_staged_matrix_amd import build as hip_build
+    w = synth.WORKLOADS["bf16_8192_nn_f32"]
+    M, N, K = w["M"], w["N"], w["K"]
+    layout = tuple(w["layouts"][0])
+    p, A, B = make_inputs(w, layout)
+    gd = DTYPE_CODE[(w["dtype"], w["out"])]
+    la = lsm.GEMM_K_CONTIG if layout[0] == "K" else lsm.GEMM_MN_CONTIG
+    lb = lsm.GEMM_K_CONTIG if layout[1] == "K" else lsm.GEMM_MN_CONTIG
+    stream = torch.cuda.current_stream()
+    ref = torch.empty(M * N, dtype=torch.float32, device="cuda")
+    h0 = lsm.gemm_create()
+    if lsm.gemm_run(h0, A, B, ref, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream) != lsm.GEMM_OK:
+        raise RuntimeError("gemm_run failed")
+    lsm.gemm_destroy(h0)
+    wgs = (M // 256) * (N // 256)
+    kt = K // 64
+    out = {}
+    for name in ("timeline", "timeline1"):
+        lib = lsm.ablation_library(name)
+        raw = ctypes.CDLL(hip_build.variant_path(name))
+        raw.lsm_pp_timeline_set.argtypes = [ctypes.c_void_p]
+        raw.lsm_pp_timeline_set.restype = ctypes.c_int
+        buf = torch.zeros(wgs * 64, dtype=torch.int64, device="cuda")
+        C = torch.empty(M * N, dtype=torch.float32, device="cuda")
+        h = lib.gemm_create()
+
+        def step():
+            if lib.gemm_run(h, A, B, C, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream) != lsm.GEMM_OK:
+                raise RuntimeError("gemm_run failed")
+
+        if raw.lsm_pp_timeline_set(buf.data_ptr()) != 0:
+            raise RuntimeError("lsm_pp_timeline_set failed")
+        try:
+            t0 = time.perf_counter()
+            while (time.perf_counter() - t0) * 1e3 < settle_ms:
+                for _ in range(20):
+                    step()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(launches):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            raw.lsm_pp_timeline_set(None)
+        lib.gemm_destroy(h)
+        ms = e0.elapsed_time(e1) / launches
+        exact = bool(torch.equal(C, ref))
+        t = buf.cpu().numpy().reshape(wgs, 8, 8).astype(np.float64)
+        res = {"ms_per_launch": round(ms, 5), "tflops": round(2.0 * M * N * K / ms / 1e9, 1),
+               "equals_library": exact}
+        print(f"{name}: {ms:.4f} ms per launch ({res['tflops']} TFLOP/s, HIP events); C equals the library's: {exact}")
+        print("  cycles per K tile, mean over workgroups | memory phase | barrier after it | MFMA issue | "
+              "wait for own loads | barrier after MFMAs | K loop | prologue (cycles) | epilogue (cycles)")
+        for grp, ws in (("group 0", slice(0, 4)), ("group 1", slice(4, 8))):
+            v = t[:, ws, :].mean(axis=(0, 1))
+            row = [round(x / kt) for x in v[:5]] + [round(v[6] / kt), round(v[5]), round(v[7])]
+            res[grp] = row
+            print(f"  {grp} | " + " | ".join(str(x) for x in row))
+        out[name] = res
+        if not exact:
+            raise RuntimeError(f"{name}: C differs from the library")
+    print(json.dumps({"probe": "ping-pong phase cycles, bf16 8192^3 NN fp32 out", "results": out}), flush=True)
+
+
 def lds_read_patterns():
     """(name, mode, 64 lane byte addresses) of the LDS read probe: the
     kernels' own fragment-read addresses (through the host build of
@@ -330,6 +408,8 @@ def main():
     ap.add_argument("--inputs", default="workload", choices=["workload", "int", "zeros", "ones"],
                     help="operand values: the workload's (default), or integers -2..2, all "
                          "zeros or all ones to show how the clock depends on the data")
+    ap.add_argument("--phase-timeline", action="store_true",
+                    help="per-phase cycles of the ping-pong kernel at 8192^3 NN (timeline builds), then exit")
     ap.add_argument("--lds-read-probe", action="store_true",
                     help="LDS reads at chosen lane addresses (for the bank-conflict counters), then exit")
     ap.add_argument("--lds-pad-probe", action="store_true",
@@ -370,6 +450,9 @@ def main():
 
     if args.lds_read_probe:
         lds_read_probe()
+        return
+    if args.phase_timeline:
+        phase_timeline()
         return
     if args.lds_pad_probe:
         lds_pad_probe()

@@ -37,6 +37,9 @@ VARIANTS = {
     "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
     "waveepi": ["-DLSM_PP_ROW_EPI=0"],      # ping-pong: C staged per wave (256/128-byte pieces) instead of per workgroup
     "oneloader": ["-DLSM_PP_SPLIT_LOADS=0"],  # ping-pong: group 0 issues every load, for every layout (no split, 2 B stages)
+    # measurement builds: the ping-pong kernel counts its phase cycles (bench.py --phase-timeline)
+    "timeline": ["-DLSM_PP_TIMELINE=1"],
+    "timeline1": ["-DLSM_PP_TIMELINE=1", "-DLSM_PP_SPLIT_LOADS=0"],
 }
 
 LAYOUT_HOST = {"": [], "_noswizzle": ["-DLSM_LDS_SWIZZLE=0"]}

@@ -260,6 +260,15 @@ static bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t
 
 extern "C" {
 
+#if LSM_PP_TIMELINE
+// Measurement builds only: install (or, with NULL, remove) the buffer the
+// ping-pong kernel writes its per-wave phase cycles to, 64 counts per
+// workgroup of the launch.  0 on success, -1 on a HIP error.
+int lsm_pp_timeline_set(void *buf) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(lsm::pp_timeline_buf), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
+}
+#endif
+
 int gemm_create(gemm_handle_t *out) {
   if (!out) return GEMM_ERR_INVALID_ARG;
   *out = nullptr;

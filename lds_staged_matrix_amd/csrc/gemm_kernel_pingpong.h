@@ -85,6 +85,21 @@ namespace lsm {
 #define LSM_PP_SPLIT_LOADS 1
 #endif
 
+// LSM_PP_TIMELINE = 1 (measurement builds only, A/B builds timeline and
+// timeline1): each wave adds up the shader-clock cycles (s_memtime) of its
+// phases and writes 8 counts to the buffer that lsm_pp_timeline_set
+// installs: memory-phase work, wait at the barrier after it, MFMA issue, wait
+// for its own loads, wait at the barrier after the MFMAs (each summed over
+// the K loop), then prologue, K loop and epilogue.  Nothing is written while
+// no buffer is installed.  The library is built with 0.
+#ifndef LSM_PP_TIMELINE
+#define LSM_PP_TIMELINE 0
+#endif
+#if LSM_PP_TIMELINE
+__device__ unsigned long long *pp_timeline_buf;
+#define PP_CLOCK() __builtin_amdgcn_s_memtime()
+#endif
+
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -101,6 +116,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
     uint32_t a_bytes, uint32_t b_bytes, int c_vec) {
   static_assert(T::WM == 2 && T::NT == 512, "two groups of four waves");
   static_assert(MF == 32 || MF == 16, "32 x 32 or 16 x 16 MFMAs");
+#if LSM_PP_TIMELINE
+  const unsigned long long t_start = PP_CLOCK();
+  unsigned long long t_first = 0, ph[5] = {0, 0, 0, 0, 0};
+#endif
   using L = AccLayout<MF>;
   constexpr int LOADERS = T::NT / 2;                     // lanes of the group loading an operand
   constexpr int ES = InT<IN>::ES;
@@ -274,6 +293,10 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
 
     typename InT<IN>::frag fa[KSTEPS][FM], fb[KSTEPS][FN];
     for (int kt = 0; kt < KT; ++kt) {
+#if LSM_PP_TIMELINE
+      const unsigned long long ta = PP_CLOCK();
+      if (kt == 0) t_first = ta;
+#endif
       // ---- memory phase M(kt)
       // The loads of this phase (none, or those the schedule gives the wave's
       // group) go into stages freed at the last barrier.  The load issue
@@ -355,7 +378,13 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
         }
       }
       wait_lds_reads();
+#if LSM_PP_TIMELINE
+      const unsigned long long tb = PP_CLOCK();
+#endif
       wg_barrier();                                      // end of M(kt)
+#if LSM_PP_TIMELINE
+      const unsigned long long tc = PP_CLOCK();
+#endif
 
       // ---- compute phase C(kt)
       __builtin_amdgcn_s_setprio(1);
@@ -375,14 +404,28 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
 #pragma unroll
         for (int j = 0; j < FN; j++) pin_acc(acc[i][j]);
       __builtin_amdgcn_s_setprio(0);
+#if LSM_PP_TIMELINE
+      const unsigned long long td = PP_CLOCK();
+      unsigned long long te = td;
+#endif
       if (group == 0) {
         wait_dma();                                      // tile kt+1 landed
+#if LSM_PP_TIMELINE
+        te = PP_CLOCK();
+#endif
         wg_barrier();                                    // end of C(kt)
       } else if (kt + 1 < KT) {
         wg_barrier();
       }
+#if LSM_PP_TIMELINE
+      const unsigned long long tf = PP_CLOCK();
+      ph[0] += tb - ta, ph[1] += tc - tb, ph[2] += td - tc, ph[3] += te - td, ph[4] += tf - te;
+#endif
     }
   }
+#if LSM_PP_TIMELINE
+  const unsigned long long t_loop = PP_CLOCK();
+#endif
 
   // The LDS is free once every wave is past its last fragment read.
   if (c_vec) {
@@ -394,6 +437,14 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_pingpong_kernel(
   } else {
     epilogue<T, OUT, MF>(C, acc, M, N, ldc, m0, n0, wm, wn, lane);
   }
+#if LSM_PP_TIMELINE
+  const unsigned long long t_end = PP_CLOCK();
+  if (pp_timeline_buf != nullptr && lane == 0) {
+    unsigned long long *o = pp_timeline_buf + ((size_t)blockIdx.x * 8 + wave) * 8;
+    for (int i = 0; i < 5; i++) o[i] = ph[i];
+    o[5] = t_first - t_start, o[6] = t_loop - t_first, o[7] = t_end - t_loop;
+  }
+#endif
 }
 
 }  // namespace lsm

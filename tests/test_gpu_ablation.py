@@ -18,7 +18,7 @@ import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1", "small2", "mfma32", "waveepi", "oneloader"]
+VARIANTS = ["noswizzle", "scalar_tr", "ring2", "noxcd", "stage1", "small2", "mfma32", "waveepi", "oneloader", "timeline", "timeline1"]
 # one shape per kernel: ping-pong (>= 256 tiles of 256), 128 x 128 tile
 # (>= 256 tiles of 128), 64 x 64 tile with two and with four LDS stages (its
 # operand panels beyond one XCD's L2), split-K ring (M <= 32)
