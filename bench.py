@@ -217,9 +217,9 @@ def lds_pad_probe(iters=4096, launches=50, repeats=9):
 
 
 
-def phase_timeline(launches=100, settle_ms=600.0):
-    """Where the ping-pong kernel's cycles go, 8192^3 NN bf16 -> fp32 on the
-    workload's inputs: the measurement builds `timeline` (the library's
+def phase_timeline(workload=HEADLINE, layout=None, launches=100, settle_ms=600.0):
+    """Where the ping-pong kernel's cycles go, on a workload that runs it
+    (8192^3 by default): the measurement builds `timeline` (the library's
     schedule) and `timeline1` (one loader group) add up, per wave, the
     shader-clock cycles of each phase over the K loop (see LSM_PP_TIMELINE in
     gemm_kernel_pingpong.h).  Each build runs `settle_ms` of launches, then
@@ -230,21 +230,24 @@ def phase_timeline(launches=100, settle_ms=600.0):
     import torch
     import lds_staged_matrix_amd as lsm
     from lds_staged_matrix_amd import build as hip_build
-    w = synth.WORKLOADS["bf16_8192_nn_f32"]
+    w = synth.WORKLOADS[workload]
     M, N, K = w["M"], w["N"], w["K"]
-    layout = tuple(w["layouts"][0])
+    layout = tuple(layout.split(",")) if layout else tuple(w["layouts"][0])
+    if M % 256 or N % 256 or (M // 256) * (N // 256) < 256:
+        sys.exit(f"--phase-timeline: {workload} does not run the ping-pong kernel")
     p, A, B = make_inputs(w, layout)
     gd = DTYPE_CODE[(w["dtype"], w["out"])]
     la = lsm.GEMM_K_CONTIG if layout[0] == "K" else lsm.GEMM_MN_CONTIG
     lb = lsm.GEMM_K_CONTIG if layout[1] == "K" else lsm.GEMM_MN_CONTIG
     stream = torch.cuda.current_stream()
-    ref = torch.empty(M * N, dtype=torch.float32, device="cuda")
+    cdt = torch.float32 if w["out"] == "f32" else torch.int16
+    ref = torch.empty(M * N, dtype=cdt, device="cuda")
     h0 = lsm.gemm_create()
     if lsm.gemm_run(h0, A, B, ref, M, N, K, p.lda, p.ldb, N, la, lb, gd, stream) != lsm.GEMM_OK:
         raise RuntimeError("gemm_run failed")
     lsm.gemm_destroy(h0)
     wgs = (M // 256) * (N // 256)
-    kt = K // 64
+    kt = (K + 63) // 64 if w["dtype"] != synth.E4M3 else (K + 127) // 128
     out = {}
     for name in ("timeline", "timeline1"):
         lib = lsm.ablation_library(name)
@@ -252,7 +255,7 @@ def phase_timeline(launches=100, settle_ms=600.0):
         raw.lsm_pp_timeline_set.argtypes = [ctypes.c_void_p]
         raw.lsm_pp_timeline_set.restype = ctypes.c_int
         buf = torch.zeros(wgs * 64, dtype=torch.int64, device="cuda")
-        C = torch.empty(M * N, dtype=torch.float32, device="cuda")
+        C = torch.empty(M * N, dtype=cdt, device="cuda")
         h = lib.gemm_create()
 
         def step():
@@ -279,6 +282,8 @@ def phase_timeline(launches=100, settle_ms=600.0):
         ms = e0.elapsed_time(e1) / launches
         exact = bool(torch.equal(C, ref))
         t = buf.cpu().numpy().reshape(wgs, 8, 8).astype(np.float64)
+        if not (t[:, :, 6] > 0).all():
+            raise RuntimeError(f"{name}: a workgroup wrote no counts")
         res = {"ms_per_launch": round(ms, 5), "tflops": round(2.0 * M * N * K / ms / 1e9, 1),
                "equals_library": exact}
         print(f"{name}: {ms:.4f} ms per launch ({res['tflops']} TFLOP/s, HIP events); C equals the library's: {exact}")
@@ -292,7 +297,8 @@ def phase_timeline(launches=100, settle_ms=600.0):
         out[name] = res
         if not exact:
             raise RuntimeError(f"{name}: C differs from the library")
-    print(json.dumps({"probe": "ping-pong phase cycles, bf16 8192^3 NN fp32 out", "results": out}), flush=True)
+    name = "".join("N" if x == ("K" if i == 0 else "MN") else "T" for i, x in enumerate(layout))
+    print(json.dumps({"probe": f"ping-pong phase cycles, {workload} {name}", "results": out}), flush=True)
 
 
 def lds_read_patterns():
@@ -452,7 +458,7 @@ def main():
         lds_read_probe()
         return
     if args.phase_timeline:
-        phase_timeline()
+        phase_timeline(args.workload, args.layout)
         return
     if args.lds_pad_probe:
         lds_pad_probe()
