@@ -35,7 +35,9 @@ VARIANTS = {
     "small2": ["-DLSM_SMALL_FOUR_STAGES=0"],  # 64 x 64 tile always double-buffered, never four stages
     "mfma32": ["-DLSM_PP_MFMA=32", "-DLSM_PP_MFMA8=32"],   # ping-pong kernel on 32x32 MFMAs (32x32x16, fp8 32x32x64)
     "poison": ["-DLSM_LDS_POISON=1"],       # LDS filled with NaN bits before each region's first use
-    "waveepi": ["-DLSM_PP_ROW_EPI=0"],      # ping-pong: C staged per wave (256/128-byte pieces) instead of per workgroup
+    # C staged per wave (ping-pong, 128 x 128 tile) or stored from the accumulators (64 x 64 tile)
+    # instead of staged for the whole workgroup
+    "waveepi": ["-DLSM_PP_ROW_EPI=0", "-DLSM_DMA_ROW_EPI=0"],
     "oneloader": ["-DLSM_PP_SPLIT_LOADS=0"],  # ping-pong: group 0 issues every load, for every layout (no split, 2 B stages)
     # measurement builds: the ping-pong kernel counts its phase cycles (bench.py --phase-timeline)
     "timeline": ["-DLSM_PP_TIMELINE=1"],

@@ -171,6 +171,15 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
 #define LSM_DMA_STAGES 2
 #endif
 
+// C stores: with 16-byte aligned C rows the kernel stages C through LDS for
+// the whole workgroup (epilogue_lds_rows: each store writes whole rows of the
+// workgroup tile, 128-512 bytes); LSM_DMA_ROW_EPI = 0, an A/B build only,
+// stages the 128 x 128 tile per wave (epilogue_lds) and stores the 64 x 64
+// tile straight from the accumulators.
+#ifndef LSM_DMA_ROW_EPI
+#define LSM_DMA_ROW_EPI 1
+#endif
+
 // Wait until at most `n` (0..3) K tiles' loads, LPT per thread each, are
 // still in flight (loads complete in issue order).
 template <int LPT>
@@ -326,9 +335,15 @@ __global__ __launch_bounds__(T::NT, 1) void lds_gemm_dma_kernel(
   }
   }
 
-  if constexpr (T::TN == 64) {
+  if constexpr (LSM_DMA_ROW_EPI) {
     if (c_vec) {
       __syncthreads();                     // every wave is past its last LDS read
+      epilogue_lds_rows<T, OUT, STAGES * STAGE, 32>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
+      return;
+    }
+  } else if constexpr (T::TN == 64) {
+    if (c_vec) {
+      __syncthreads();
       epilogue_lds<T, OUT, STAGES * STAGE>(C, acc, smem, M, N, ldc, m0, n0, wm, wn, wave, lane);
       return;
     }

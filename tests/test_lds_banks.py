@@ -626,19 +626,31 @@ def test_epilogue_staging_writes_and_reads_are_conflict_free(layouts, mf, esz):
         assert b128_degree(addrs) == 1        # and in the measured two-pass form of ds_read_b128
 
 
-# The ping-pong kernel's workgroup-row staging: rows of the 256-column
-# workgroup tile (1 KiB of fp32, 512 bytes of bf16/fp16), written by every
+# The workgroup-row staging of the ping-pong and direct-to-LDS kernels: rows of
+# the workgroup tile (256 columns: 1 KiB of fp32, 512 bytes of 16-bit output;
+# 128 columns: 512 / 256 bytes; 64 columns: 256 / 128 bytes), written by every
 # accumulator register of the tile's waves, read back 16 bytes per lane.
+# (BM, BN, TM, TN, WM, WN, LDS bytes the kernel owns, MFMA shapes)
+ROW_EPI_TILES = {
+    "pingpong": (256, 256, 128, 64, 2, 4, 2 * 65536, (32, 16)),
+    "dma128": (128, 128, 64, 64, 2, 2, 2 * 32768, (32,)),
+    "dma64": (64, 64, 32, 32, 2, 2, 2 * 16384, (32,)),
+    "dma64_four_stages": (64, 64, 32, 32, 2, 2, 4 * 16384, (32,)),
+}
+ROW_EPI_CASES = [(t, mf) for t, v in ROW_EPI_TILES.items() for mf in v[7]]
 
-@pytest.mark.parametrize("mf", [32, 16])
+
+@pytest.mark.parametrize("tile,mf", ROW_EPI_CASES)
 @pytest.mark.parametrize("esz", [4, 2])
-def test_workgroup_row_staging_is_conflict_free(layouts, mf, esz):
+def test_workgroup_row_staging_is_conflict_free(layouts, tile, mf, esz):
     lib = layouts["swizzled"]
-    rowb, tm, tn = 256 * esz, 128, 64
-    rp = min(2 * 65536 // rowb, 256)                       # rows per pass in 128 KiB
+    bm, bn, tm, tn, wms, wns, lds, _ = ROW_EPI_TILES[tile]
+    rowb = bn * esz
+    rp = min(lds // rowb, bm)                              # rows per pass
+    assert rp % tm == 0
     off = lambda row, chunk: lib.lsm_epi_row_stage_offset(row, chunk, rowb, mf, esz)
     for wm in range(rp // tm):                             # the waves of one pass
-        for wn in range(4):
+        for wn in range(wns):
             for i in range(tm // mf):
                 for j in range(tn // mf):
                     for r in range(16 if mf == 32 else 4):
@@ -656,12 +668,13 @@ def test_workgroup_row_staging_is_conflict_free(layouts, mf, esz):
         assert degree(addrs, 16) == 1 and b128_degree(addrs) == 1
 
 
-@pytest.mark.parametrize("mf", [32, 16])
+@pytest.mark.parametrize("tile,mf", ROW_EPI_CASES)
 @pytest.mark.parametrize("esz", [4, 2])
-def test_workgroup_row_staging_is_a_permutation_of_each_row(layouts, mf, esz):
+def test_workgroup_row_staging_is_a_permutation_of_each_row(layouts, tile, mf, esz):
     lib = layouts["swizzled"]
-    rowb = 256 * esz
-    for row in range(256):
+    bm, bn = ROW_EPI_TILES[tile][:2]
+    rowb = bn * esz
+    for row in range(bm):
         got = sorted(lib.lsm_epi_row_stage_offset(row, c, rowb, mf, esz) for c in range(rowb // 16))
         assert got == [row * rowb + 16 * c for c in range(rowb // 16)]
 
