@@ -44,6 +44,9 @@
 // Tiles 0 and 1 come with the prologue (split: each group its operand).
 // Every wave waits for its own LDS reads before the barrier that ends its
 // memory phase, and a tile is complete at the barrier before its first read.
+// A wave's vmcnt covers only its own quarter of its group's loads, so even
+// the loading group reads a tile only after a barrier that follows all four
+// waits: group 0's wait stays at the end of C(t), before barrier 2t+2.
 //
 // The LDS layout, the swizzle on the global side of the loads, the edge
 // handling through buffer range checks and the inline-assembly loads are

@@ -8,7 +8,14 @@ for: no read of a tile before its loads have been waited for by the loading
 group and a barrier has followed; no load into a stage before every read of
 the tile that held it has been followed by a barrier.  It also rejects the
 schedules one small change away from the kernel's (B in two stages, a missing
-wait, loads one tile further ahead), so the checks have teeth."""
+wait, loads one tile further ahead, group 0's wait moved past the barrier that
+ends its compute phase), so the checks have teeth.
+
+A group is four waves, and each loads a quarter of its tile; a wave's wait
+covers its own loads only, while its fragment reads take every quarter.  So a
+read is safe only after a barrier that follows the loading waves' waits, even
+in the loading group: the checker counts a load as visible from the epoch
+after its wait, never in the same epoch."""
 import itertools
 
 import pytest
@@ -18,9 +25,11 @@ import pytest
 # ("barrier",)
 
 
-def split_schedule(KT, b_stages=3, b_ahead=2, group1_waits=True):
+def split_schedule(KT, b_stages=3, b_ahead=2, group1_waits=True, g0_wait_after_barrier=False):
     """The split-load schedule as the kernel runs it; the keyword arguments
-    plant the mistakes the tests expect to be caught."""
+    plant the mistakes the tests expect to be caught (g0_wait_after_barrier:
+    group 0 waits for A of tile t+1 at the start of M(t+1), just before its
+    own first read, instead of before the barrier that ends C(t))."""
     a_st = lambda t: t % 2
     b_st = lambda t: t % b_stages
     g = {0: [], 1: []}
@@ -34,6 +43,8 @@ def split_schedule(KT, b_stages=3, b_ahead=2, group1_waits=True):
     for kt in range(KT):
         for grp in (0, 1):
             ev = g[grp]
+            if grp == 0 and kt >= 1 and g0_wait_after_barrier:
+                ev.append(("wait", 0))
             ev += [("read", "A", kt, a_st(kt)), ("read", "B", kt, b_st(kt))]
             if grp == 0 and kt >= 1 and kt + 1 < KT:
                 ev.append(("load", "A", kt + 1, a_st(kt + 1)))
@@ -44,7 +55,8 @@ def split_schedule(KT, b_stages=3, b_ahead=2, group1_waits=True):
                 ev.append(("wait", 1 if loaded else 0))
             ev.append(("barrier",))                           # end of M(kt)
             if grp == 0:
-                ev.append(("wait", 0))                        # A of tile kt+1 landed
+                if not g0_wait_after_barrier:
+                    ev.append(("wait", 0))                    # A of tile kt+1 landed
                 ev.append(("barrier",))                       # end of C(kt)
             elif kt + 1 < KT:
                 ev.append(("barrier",))
@@ -158,6 +170,13 @@ def test_group1_must_wait_for_its_loads():
 def test_b_loads_three_tiles_ahead_overwrite_a_live_stage():
     probs = check(split_schedule(7, b_ahead=3), 7)
     assert any("still read there" in p for p in probs), probs
+
+
+def test_group0_wait_must_precede_the_barrier_before_its_own_reads():
+    """Moving group 0's wait off its compute phase, to just before its own
+    reads, leaves the other waves' quarters of the tile unsynchronised."""
+    probs = check(split_schedule(6, g0_wait_after_barrier=True), 6)
+    assert any(p.startswith("group 0 reads ('A', 1)") for p in probs), probs
 
 
 def test_one_loader_with_one_stage_is_rejected():
