@@ -10,12 +10,15 @@ Prints ONE JSON line on stdout.  Extra per-run detail goes to stderr.
   python bench.py --profile-run      # a few launches only, for rocprofv3
   python bench.py --copy-calibration # one plain 1 GiB device copy, for rocprofv3 --pmc
   python bench.py --variant noswizzle # an A/B build with one design choice changed
+  python bench.py --telemetry ...     # the same run as a child process, with socket
+                                      # power and GFX clock sampled once a second
 """
 import argparse
 import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -385,7 +388,66 @@ def lds_read_probe(iters=2000, launches=2):
     print(json.dumps({"probe": "lds lane-address reads, one wave", "results": rows}), flush=True)
 
 
+def parse_amd_smi(text):
+    """(socket power in W, GFX_0 clock in MHz) from `amd-smi metric -p -c
+    --json` output, or None when the reading has neither."""
+    try:
+        d = json.loads(text)
+        d = d[0] if isinstance(d, list) else d
+        if isinstance(d, dict) and "gpu_data" in d:
+            d = d["gpu_data"][0]
+        val = lambda x: x.get("value") if isinstance(x, dict) else x
+        w, c = val(d["power"]["socket_power"]), val(d["clock"]["gfx_0"]["clk"])
+        return (float(w), float(c)) if isinstance(w, (int, float)) and isinstance(c, (int, float)) else None
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
+def summarize_telemetry(samples, loaded_w=600.0):
+    """Ranges over the samples taken under load: those above `loaded_w`
+    watts, without the first and the last (the clock still moving at the
+    start, the load ending during the last second)."""
+    loaded = [x for x in samples if x[1] is not None and x[1] > loaded_w][1:-1]
+    if not loaded:
+        return {"n": 0}
+    w = [x[1] for x in loaded]
+    c = [x[2] for x in loaded]
+    return {"n": len(loaded), "socket_power_w": [min(w), max(w)], "gfx_clk_mhz": [min(c), max(c)],
+            "gfx_clk_mhz_mean": round(sum(c) / len(c), 1)}
+
+
+def run_with_telemetry(argv):
+    """Run this benchmark with `argv` as a child process and read amd-smi
+    once a second while it runs.  This process itself never touches the GPU.
+    Prints the child's JSON line with a `telemetry` object added and returns
+    the child's exit status."""
+    child = subprocess.Popen([sys.executable, os.path.abspath(__file__)] + argv,
+                             stdout=subprocess.PIPE, text=True)
+    samples, t0 = [], time.time()
+    while child.poll() is None:
+        time.sleep(1.0)
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                               text=True, timeout=30)
+            reading = parse_amd_smi(r.stdout)
+        except (OSError, subprocess.TimeoutExpired):
+            reading = None
+        samples.append([round(time.time() - t0, 1)] + (list(reading) if reading else [None, None]))
+        log(f"telemetry {samples[-1]}")
+    out = child.stdout.read()
+    lines = [l for l in out.strip().splitlines() if l.startswith("{")]
+    if child.returncode != 0 or not lines:
+        return child.returncode or 1
+    line = json.loads(lines[-1])
+    line["telemetry"] = {"source": "amd-smi metric -p -c --json, once a second",
+                         "samples_t_s_w_mhz": samples, "loaded": summarize_telemetry(samples)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
+    if "--telemetry" in sys.argv[1:]:
+        sys.exit(run_with_telemetry([a for a in sys.argv[1:] if a != "--telemetry"]))
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # 500 untimed and 100 timed launches, the ladder page's test configuration
@@ -428,6 +490,9 @@ def main():
                     help="skip the timing of the steps captured in one HIP graph")
     ap.add_argument("--no-flushed", action="store_true",
                     help="skip the 20 launches timed with the caches flushed before each")
+    ap.add_argument("--telemetry", action="store_true",
+                    help="run the rest of the command as a child process and add amd-smi "
+                         "socket power and GFX clock readings, once a second, to its JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

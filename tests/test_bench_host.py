@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard, the readers of the
 committed rocprofv3 summaries, and the oracle CPU-baseline leg."""
+import json
 import os
 import re
 import subprocess
@@ -81,3 +82,37 @@ def test_lds_read_probe_patterns_cover_the_measured_cases():
     text = open(os.path.join(ROOT, "profiles", "lds_bank_passes_read_probe.txt")).read()
     for n in names:
         assert n in text, n
+
+
+def test_amd_smi_reading_is_parsed_from_its_json_forms():
+    one = {"power": {"socket_power": {"value": 1398, "unit": "W"}},
+           "clock": {"gfx_0": {"clk": {"value": 1805, "unit": "MHz"}}}}
+    assert bench.parse_amd_smi(json.dumps(one)) == (1398.0, 1805.0)
+    assert bench.parse_amd_smi(json.dumps([one])) == (1398.0, 1805.0)
+    assert bench.parse_amd_smi(json.dumps({"gpu_data": [one]})) == (1398.0, 1805.0)
+    plain = {"power": {"socket_power": 700}, "clock": {"gfx_0": {"clk": 2400}}}
+    assert bench.parse_amd_smi(json.dumps(plain)) == (700.0, 2400.0)
+    assert bench.parse_amd_smi("") is None
+    assert bench.parse_amd_smi(json.dumps({"power": {"socket_power": "N/A"},
+                                           "clock": {"gfx_0": {"clk": 2400}}})) is None
+
+
+def test_telemetry_ranges_keep_the_loaded_samples_only():
+    samples = [[1.0, 300.0, 2100.0], [2.0, 1300.0, 2000.0], [3.0, 1398.0, 1810.0],
+               [4.0, 1400.0, 1790.0], [5.0, None, None], [6.0, 1390.0, 1800.0], [7.0, 900.0, 2300.0],
+               [8.0, 250.0, 2100.0]]
+    s = bench.summarize_telemetry(samples)
+    # above 600 W: t = 2, 3, 4, 6, 7; the first and the last of those are dropped
+    assert s["n"] == 3
+    assert s["socket_power_w"] == [1390.0, 1400.0]
+    assert s["gfx_clk_mhz"] == [1790.0, 1810.0]
+    assert bench.summarize_telemetry([[1.0, 100.0, 2000.0]]) == {"n": 0}
+
+
+def test_telemetry_run_passes_the_child_status_through():
+    # the child refuses more than one GPU before touching any; no JSON line
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--telemetry", "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
